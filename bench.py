@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention decode hot path on one MI355X.
+
+One step = one batched decode step of the whole model depth: for every layer,
+the cache write of the step's new K/V rows (one per sequence) followed by
+paged-attention decode over every sequence's context. Default workload: the
+Qwen3-0.6B-shaped batch (60 sequences, contexts uniform in [64, 256], 16 q /
+8 kv heads, head_dim 128, bf16, 16-token blocks, 28 layers each with its own
+pool). Inputs are synthetic, seeded, and resident in HBM before timing.
+
+Prints ONE JSON line:
+  value        KV bytes read per step / step time (GB/s), all layers
+  roofline     the decode kernel alone: algorithmic bytes per launch / mean
+               launch time from HIP events, against 8 TB/s HBM peak
+  cpu_baseline the fp64 oracle on the host, on a bounded sample of layers
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--partition P]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+
+WORKLOAD_TEXT = {
+    "qwen3": "Qwen3-0.6B-shaped decode step: 60 seqs, context U[64,256], 16 q / 8 kv heads, "
+             "head_dim 128, bf16, block 16, 28 layers x (cache write of 60 rows + decode)",
+    "tinyllama": "TinyLlama-1.1B-shaped decode step: 256 seqs, context U[512,2048], 32 q / 4 kv "
+                 "heads, head_dim 64, fp16, block 16, cache write of 256 rows + decode, 3 pools rotated",
+    "llama7b_long": "Llama/Mistral-7B-shaped long-context decode step: 32 seqs x 32768 tokens, 32 q / "
+                    "8 kv heads, head_dim 128, bf16, 16 seqs share a 16384-token prefix",
+    "skewed": "Skewed mixed batch: 512 seqs, lognormal contexts (one of 131072, 64 of 1), 16 q / 8 kv "
+              "heads, head_dim 128, bf16, cache write of 512 rows + decode",
+    "tiny": "Tiny paged decode: 4 seqs, contexts {1,17,32,45}, 4 q / 2 kv heads, head_dim 64, fp16",
+}
+POOL_SETS = {"tinyllama": 3}   # extra pool copies so repeated steps do not hit in the 256 MB MALL
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library choice)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence / KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_206_amd as mvk
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.make(args.workload, value_device="cuda")   # seeded; values drawn on the GPU
+    nsets = POOL_SETS.get(args.workload, 1)
+    layers = list(wl.layers)
+    for extra in range(1, nsets):
+        w2 = W.make(args.workload, seed=W.SEEDS[args.workload] + 100 * extra, value_device="cuda")
+        layers += w2.layers   # same structure (structure seed unchanged), fresh values
+    nlayers_step = len(wl.layers)
+    bt = wl.block_tables.to(dev)
+    cl = wl.context_lens.to(dev)
+    slots = wl.slot_mapping.to(dev)
+    S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    maxlen = wl.max_context_len
+    ws_bytes, part = mvk.workspace_size(S, Hq, Hkv, D, maxlen, args.partition)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(l.q) for l in layers]
+    torch.cuda.synchronize()
+
+    def layer_call(li, write=True):
+        l = layers[li]
+        if write:
+            mvk.reshape_and_cache(l.key, l.value, l.k_cache, l.v_cache, slots)
+        mvk.paged_attention_decode(l.q, l.k_cache, l.v_cache, bt, cl, wl.scale,
+                                   max_context_len=maxlen, out=outs[li], partition_tokens=part,
+                                   workspace=ws)
+
+    step_counter = [0]
+
+    def step():
+        base = (step_counter[0] % nsets) * nlayers_step
+        for li in range(nlayers_step):
+            layer_call(base + li)
+        step_counter[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # ---- decode kernel alone, HIP events around every launch on its stream
+    stream = torch.cuda.current_stream(dev)
+    n_ev = args.steps * nlayers_step
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_ev)]
+    for i in range(n_ev):
+        li = (i // nlayers_step % nsets) * nlayers_step + i % nlayers_step
+        ev[i][0].record(stream)
+        layer_call(li, write=False)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    launch_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    # back-to-back decode launches, one event pair around the whole run
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n_ev):
+        layer_call((i // nlayers_step % nsets) * nlayers_step + i % nlayers_step, write=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b_us = e0.elapsed_time(e1) * 1e3 / n_ev
+
+    # ---- byte accounting (per layer), from the workload's structure
+    lens = wl.context_lens.to(torch.int64)
+    e = 2
+    kv_logical = int(lens.sum()) * Hkv * D * e * 2
+    kv_unique_tokens = unique_token_rows(wl) * Hkv * D * e * 2    # shared prefix blocks once
+    table_bytes = int(((lens + 15) // 16).sum()) * 4
+    qo_bytes = 2 * S * Hq * D * e
+    decode_alg = kv_unique_tokens + qo_bytes + table_bytes + S * 4
+    write_alg = 2 * 2 * S * Hkv * D * e + S * 4          # read new rows + write slots (K and V)
+    step_kv = kv_logical * nlayers_step
+    step_s = ms_per_step / 1e3
+    value = step_kv / step_s / 1e9
+    achieved = decode_alg / (launch_us * 1e-6) / 1e9
+
+    result = {
+        "metric": "paged-decode KV read GB/s (% of MI355X HBM peak); decode tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q, random block tables)",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.workload],
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "block_size": 16, "layers_per_step": nlayers_step, "max_context_len": maxlen,
+            "partition_tokens": part, "pool_sets": nsets,
+        },
+        "pct_hbm_peak": round(100.0 * (decode_alg + write_alg) * nlayers_step / step_s / 1e9
+                              / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(S / step_s, 1),
+        "kv_bytes_per_step": step_kv,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_partition_kernel",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "alg_bytes_per_launch": decode_alg,
+            "launch_us_events": round(launch_us, 3),
+            "launch_us_back_to_back": round(b2b_us, 3),
+        },
+    }
+
+    if not args.no_cpu and args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(wl, layers[:nlayers_step], args.cpu_seconds,
+                                              kv_logical)
+    print(json.dumps(result), flush=True)
+
+
+def unique_token_rows(wl):
+    """Token rows decode must read at least once: every distinct physical block
+    counts the largest number of its rows any sequence uses."""
+    rows = {}
+    bt = wl.block_tables.tolist()
+    for s, L in enumerate(wl.context_lens.tolist()):
+        for i in range(-(-L // 16)):
+            b = bt[s][i]
+            rows[b] = max(rows.get(b, 0), min(16, L - 16 * i))
+    return sum(rows.values())
+
+
+def cpu_baseline(wl, layers, budget_s, kv_logical_per_layer):
+    """Time the fp64 oracle (as it stands) on the host: cache write + decode of
+    whole layers, until the time budget is spent (at least one layer)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    bt = wl.block_tables.numpy()
+    cl = wl.context_lens.numpy()
+    slots = wl.slot_mapping.numpy() if wl.slot_mapping is not None else None
+    spent, done = 0.0, 0
+    with threadpool_limits(limits=1):
+        spent, done = _time_oracle(oracle, wl, layers, bits, bt, cl, slots, budget_s)
+    gbs = kv_logical_per_layer * done / spent / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {len(layers)} layers of the same step (cache write + decode, all "
+                  f"{wl.num_seqs} seqs), numpy fp64, BLAS limited to 1 thread, host copy untimed",
+        "seconds": round(spent, 3),
+        "tokens_per_s": round(wl.num_seqs * done / len(layers) / spent, 3),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def _time_oracle(oracle, wl, layers, bits, bt, cl, slots, budget_s):
+    spent, done = 0.0, 0
+    for layer in layers:
+        host = [bits(t) for t in (layer.q, layer.k_cache, layer.v_cache)]
+        kv_new = (bits(layer.key), bits(layer.value)) if layer.key is not None else None
+        t0 = time.perf_counter()
+        kc, vc = host[1], host[2]
+        if kv_new is not None:
+            kc, vc = oracle.cache_write(kc, vc, kv_new[0], kv_new[1], slots)
+        oracle.paged_decode(host[0], kc, vc, bt, cl, wl.scale, wl.dtype)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    return spent, done
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * mvk.h - C ABI of the MI355X (gfx950) paged KV-cache attention library.
+ *
+ * Two operations make up one decode step of a paged KV cache:
+ *
+ *   mvk_reshape_and_cache       scatter the step's new K/V rows into their
+ *                               physical slots of the block pools;
+ *   mvk_paged_attention_decode  each sequence's single new query token attends
+ *                               over its whole cached context, read block by
+ *                               block through its block table.
+ *
+ * Where the operations come from (web pages on small vLLM re-implementations):
+ *   - "从零手写 vLLM 核心：mini-vllm 项目深度解析", section "2. 分页KV缓存（PagedAttention）":
+ *     the KV cache is cut into fixed 16-token blocks managed like pages of
+ *     virtual memory, which lets sequences share physical blocks (prefix cache);
+ *   - same page, "关键工程决策", item 1: every layer reads its own cache length;
+ *     item 2: in steady state every running request is in one batched decode;
+ *     item 3: K and V pools are separate, layer-first, with the block dimension
+ *     ahead of the KV-head dimension, and attention receives views of them;
+ *   - micro-vLLM wiki, feature list and API example: the attention operator is
+ *     a swappable backend (this library is one), block_size = 16.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers to tensors are DEVICE pointers owned by the caller. The library
+ *     allocates nothing, keeps no state between calls and is thread-safe.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     asynchronously; MVK_OK means "arguments valid and kernels launched".
+ *     A fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is launched and nothing is written.
+ *   - Tensors are dense and row-major; every tensor pointer must be 16-byte
+ *     aligned.
+ *   - dtype: MVK_F16 (IEEE binary16) or MVK_BF16 (bfloat16). q, the pools,
+ *     key/value and out all share it.
+ *   - Pool layout (one layer): [num_blocks, block_size, num_kv_heads, head_dim].
+ *     Token t of sequence s lives in physical block block_tables[s][t / 16] at
+ *     offset t % 16. A flat slot number is block * 16 + offset.
+ *   - Device-side index contents (block ids, slots, lengths) are not checked on
+ *     the host. The kernels never access memory outside the buffers described
+ *     by the size arguments: an out-of-range block id is read as block 0 and an
+ *     out-of-range slot is not written; the affected output is then unspecified.
+ */
+#ifndef MVK_H
+#define MVK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MVK_ABI_VERSION 1
+
+typedef enum mvk_status {
+    MVK_OK = 0,
+    MVK_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misaligned tensor */
+    MVK_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, group size, block size */
+    MVK_ERR_WORKSPACE_TOO_SMALL = 3,
+    MVK_ERR_HIP = 4                 /* a HIP launch reported an error */
+} mvk_status;
+
+typedef enum mvk_dtype {
+    MVK_F16 = 0,
+    MVK_BF16 = 1
+} mvk_dtype;
+
+/* Version of this ABI (MVK_ABI_VERSION of the built library). */
+int32_t mvk_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* mvk_status_string(int32_t status);
+
+/*
+ * mvk_reshape_and_cache - write one step's new K and V rows into the pools.
+ *
+ * Defines: for every i < num_tokens with s = slot_mapping[i] >= 0,
+ *   k_cache[s / 16][s % 16][:][:] = key[i][:][:]  and the same for V.
+ * The copy is raw (no conversion), so the pools receive the exact bits.
+ * (Paged cache with fixed 16-token blocks: mini-vllm write-up, section
+ * "2. 分页KV缓存（PagedAttention）"; pool layout: "关键工程决策", item 3.)
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_dim], dtype, read only.
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim], dtype;
+ *   v_cache       only the addressed rows are written.
+ *   slot_mapping  int32 [num_tokens]; negative = padding, skipped. A slot at or
+ *                 past num_blocks * block_size is skipped. Two tokens with the
+ *                 same slot leave that row holding one of them (unspecified).
+ *   block_size    must be 16.  head_dim: 64 or 128.  num_tokens == 0 is a no-op.
+ * Errors: MVK_ERR_INVALID_ARGUMENT (null/misaligned pointers, negative sizes,
+ * bad dtype), MVK_ERR_UNSUPPORTED (block_size, head_dim), MVK_ERR_HIP.
+ */
+int32_t mvk_reshape_and_cache(const void* key, const void* value,
+                              void* k_cache, void* v_cache,
+                              const int32_t* slot_mapping,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks,
+                              int32_t dtype, void* stream);
+
+/*
+ * mvk_paged_attention_workspace_size - bytes of scratch that
+ * mvk_paged_attention_decode needs for these sizes.
+ *
+ * Long contexts are cut into partitions of `partition_tokens` tokens (a
+ * multiple of 16; 0 lets the library choose from num_seqs, num_kv_heads and
+ * max_context_len). When a sequence spans more than one partition, each
+ * partition's partial softmax state (running max, denominator, normalised
+ * output; float32) goes to the workspace and a second kernel merges them.
+ *
+ *   *workspace_bytes          receives the size (0 when no split is needed).
+ *   *chosen_partition_tokens  receives the partition length that the decode
+ *                             call will use for the same arguments (may be NULL).
+ * Errors: as for mvk_paged_attention_decode's size checks.
+ */
+int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t max_context_len, int32_t partition_tokens,
+                                           size_t* workspace_bytes,
+                                           int32_t* chosen_partition_tokens);
+
+/*
+ * mvk_paged_attention_decode - one batched decode step of paged attention.
+ *
+ * Defines, for every sequence s, query head j and d < head_dim, with
+ * L = context_lens[s], g = num_q_heads / num_kv_heads and h = j / g
+ * (consecutive query heads share a KV head):
+ *   z_t        = scale * sum_d q[s][j][d] * K_t[h][d]        for t < L,
+ *   out[s][j]  = sum_t softmax(z)_t * V_t[h]
+ * where K_t / V_t are token t's rows fetched through block_tables[s]. The new
+ * token of this step must already be in the pools (mvk_reshape_and_cache first)
+ * and counted in L. L == 0 gives an all-zero row. Arithmetic is float32
+ * (products, logits, softmax, accumulation); out is rounded to nearest-even.
+ * (Method: mini-vllm write-up, "2. 分页KV缓存（PagedAttention）" and
+ * "关键工程决策" items 1-3; micro-vLLM wiki, paged-attention backend.)
+ *
+ *   out           [num_seqs, num_q_heads, head_dim], dtype, written.
+ *   q             [num_seqs, num_q_heads, head_dim], dtype.
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim], dtype.
+ *   v_cache
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entries past
+ *                 ceil(L / 16) are never read (any value).
+ *   context_lens  int32 [num_seqs]; each must be <= max_context_len (tokens
+ *                 past it are ignored).
+ *   max_context_len  host-side upper bound of context_lens; sizes the split.
+ *                 Must be <= max_blocks_per_seq * 16.
+ *   scale         finite float multiplier of the raw dot products.
+ *   partition_tokens  0 = library choice, else a multiple of 16 in [16, 65536].
+ *   workspace     device scratch of workspace_bytes (from
+ *                 mvk_paged_attention_workspace_size with the same sizes and
+ *                 partition_tokens); may be NULL when that size is 0. Owned by
+ *                 the caller; contents need no initialisation; must not be
+ *                 shared by calls that may run concurrently.
+ *   head_dim 64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
+ *   block_size 16.  num_seqs == 0 is a no-op.
+ * Unused pool slots and the unread tail of a sequence's last block may hold
+ * any bits, NaN included: they do not reach the output.
+ * The output does not depend on the order in which the GPU runs work items:
+ * repeated calls with the same inputs give identical bits.
+ * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED,
+ * MVK_ERR_WORKSPACE_TOO_SMALL, MVK_ERR_HIP.
+ */
+int32_t mvk_paged_attention_decode(void* out, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len,
+                                   float scale, int32_t dtype, int32_t partition_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MVK_H */

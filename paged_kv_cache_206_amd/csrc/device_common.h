@@ -1,0 +1,75 @@
+// Device helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mvk {
+
+constexpr int kBlockTokens = 16;  // tokens per KV block
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// Storage types. DT 0 = IEEE binary16, DT 1 = bfloat16; both are 16-bit words.
+template <int DT> struct Elem;
+
+template <> struct Elem<0> {
+  // a.lo*b.lo + a.hi*b.hi + c, products and sum in float32 (v_dot2c_f32_f16)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                  false);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  // float32 -> binary16, round to nearest even
+  static __device__ __forceinline__ uint16_t round(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
+
+template <> struct Elem<1> {
+  // a.lo*b.lo + a.hi*b.hi + c in float32 (v_dot2c_f32_bf16)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                           __builtin_bit_cast(bf162_t, b), c, false);
+  }
+  // bfloat16 is the top half of a float32: widening is a shift / mask
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  // float32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+  static __device__ __forceinline__ uint16_t round(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-lane moves inside a 16-lane DPP row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15-i within each 16 lanes
+
+// Sum over each aligned group of N lanes (N = 8 or 16); every lane of the
+// group receives the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  x += dpp_mov<kDppQuadXor1>(x);
+  x += dpp_mov<kDppQuadXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  if constexpr (N == 16) x += dpp_mov<kDppRowMirror>(x);
+  return x;
+}
+
+}  // namespace mvk

@@ -1,0 +1,36 @@
+// Internal launchers behind the C ABI (host side). Arguments are already
+// validated by the entry points in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mvk {
+
+hipError_t launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
+                              const int32_t* slot_mapping, int32_t num_tokens, int32_t row_vecs,
+                              int64_t num_slots, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_ml;  // [S, Hq, num_parts, 2] (running max in log2 units, denominator)
+  float* ws_o;   // [S, Hq, num_parts, D] normalised partial outputs
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int32_t num_blocks, max_blocks_per_seq, max_context_len;
+  int32_t partition_tokens, num_parts;
+  float scale_log2;  // scale * log2(e): logits are kept in base-2 units
+  int32_t dtype;
+};
+
+// Kernel variants are instantiated for these group sizes and head dims.
+bool decode_supported(int32_t head_dim, int32_t group);
+
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace mvk

@@ -7,5 +7,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def pytest_sessionstart(session):
+    """Build the HIP library in-tree if it is not there yet (a fresh checkout)."""
+    lib = os.path.join(ROOT, "paged_kv_cache_206_amd", "libmvk.so")
+    if not os.path.exists(lib):
+        from paged_kv_cache_206_amd.build import build
+        build()
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
