@@ -144,7 +144,7 @@ int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads
  *   max_context_len  host-side upper bound of context_lens; sizes the split.
  *                 Must be <= max_blocks_per_seq * 16.
  *   scale         finite float multiplier of the raw dot products.
- *   partition_tokens  0 = library choice, else a multiple of 16 in [16, 65536].
+ *   partition_tokens  0 = library choice, else a multiple of 16 in [16, 4096].
  *   workspace     device scratch of workspace_bytes (from
  *                 mvk_paged_attention_workspace_size with the same sizes and
  *                 partition_tokens); may be NULL when that size is 0. Owned by

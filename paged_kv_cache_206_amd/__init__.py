@@ -2,7 +2,7 @@
 
 Argument marshalling only: torch supplies device memory and the current HIP
 stream; every step of the computation runs in the library's HIP kernels. There
-is no fallback: if libmvk.so is missing the import fails with instructions.
+is no fallback: if libmvk.so is missing, the first call fails with instructions.
 
     reshape_and_cache(key, value, k_cache, v_cache, slot_mapping)
     paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
@@ -68,18 +68,27 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-_lib = load_library()
+_LIB = None
 
-if _lib.mvk_abi_version() != 1:
-    raise ImportError(f"libmvk ABI version {_lib.mvk_abi_version()} != 1")
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use, so that the build module can be
+    imported before anything is built)."""
+    global _LIB
+    if _LIB is None:
+        loaded = load_library()
+        if loaded.mvk_abi_version() != 1:
+            raise ImportError(f"libmvk ABI version {loaded.mvk_abi_version()} != 1")
+        _LIB = loaded
+    return _LIB
 
 
 def status_string(status: int) -> str:
-    return _lib.mvk_status_string(status).decode()
+    return lib().mvk_status_string(status).decode()
 
 
 def abi_version() -> int:
-    return _lib.mvk_abi_version()
+    return lib().mvk_abi_version()
 
 
 def _check(func: str, status: int) -> None:
@@ -127,7 +136,7 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
     if value.shape != key.shape or v_cache.shape != k_cache.shape or (hkv2, d2) != (hkv, d) \
             or slot_mapping.shape[0] != T:
         raise ValueError("inconsistent shapes")
-    st = _lib.mvk_reshape_and_cache(key.data_ptr(), value.data_ptr(), k_cache.data_ptr(),
+    st = lib().mvk_reshape_and_cache(key.data_ptr(), value.data_ptr(), k_cache.data_ptr(),
                                     v_cache.data_ptr(), slot_mapping.data_ptr(), T, hkv, d, bs,
                                     nb, _dtype_code(key), _stream(key.device))
     _check("mvk_reshape_and_cache", st)
@@ -138,7 +147,7 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
     """(workspace bytes, partition length) the decode call will use."""
     nbytes = ctypes.c_size_t(0)
     chosen = ctypes.c_int32(0)
-    st = _lib.mvk_paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+    st = lib().mvk_paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                  max_context_len, partition_tokens,
                                                  ctypes.byref(nbytes), ctypes.byref(chosen))
     _check("mvk_paged_attention_workspace_size", st)
@@ -181,7 +190,7 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         _require(workspace, "workspace", dtype=torch.uint8)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    st = _lib.mvk_paged_attention_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+    st = lib().mvk_paged_attention_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
                                          v_cache.data_ptr(), block_tables.data_ptr(),
                                          context_lens.data_ptr(), S, hq, hkv, d, bs, nb,
                                          block_tables.shape[1], max_context_len, float(scale),

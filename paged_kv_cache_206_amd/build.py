@@ -36,8 +36,10 @@ COMMON_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libmvk.so; returns its path."""
+def build(verbose: bool = False, defines=()) -> str:
+    """Compile every source and link libmvk.so; returns its path. `defines`
+    adds -D flags (MVK_TUNING builds a variant whose planner honours the
+    MVK_TUNE_P / MVK_TUNE_W environment variables, for tuning sweeps)."""
     cc = hipcc()
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not sources:
@@ -46,7 +48,8 @@ def build(verbose: bool = False) -> str:
         objs = []
         for src in sources:
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [cc, *COMMON_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+            cmd = [cc, *COMMON_FLAGS, *("-D" + d for d in defines), "-I", os.path.join(ROOT, "include"),
+                   "-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
@@ -62,7 +65,8 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     try:
-        path = build(verbose="-v" in sys.argv)
+        defs = [a.split("=", 1)[1] for a in sys.argv[1:] if a.startswith("--define=")]
+        path = build(verbose="-v" in sys.argv, defines=defs)
     except subprocess.CalledProcessError as e:
         if e.stderr:
             sys.stderr.write(e.stderr.decode(errors="replace"))

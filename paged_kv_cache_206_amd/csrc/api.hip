@@ -2,36 +2,67 @@
 // Nothing here touches the GPU before every argument has been checked.
 #include <math.h>
 #include <stdint.h>
+#ifdef MVK_TUNING
+#include <stdlib.h>
+#endif
 
-#include "../../include/mvk.h"
+#include "mvk.h"
 #include "launch.h"
 
 namespace {
 
 constexpr int32_t kBlock = 16;
-constexpr int32_t kMaxPartition = 65536;
+constexpr int32_t kMinWaves = 4;
+// a wave prefetches its table entries into one VGPR: at most 64 blocks per
+// wave, so a partition holds at most 64 * 16 * (waves per workgroup) tokens
+constexpr int32_t kMaxPartition = 64 * 16 * kMinWaves;
 constexpr int32_t kMaxGridYZ = 65535;
+// A multi-partition batch whose dense (partition, KV head, sequence) grid
+// would exceed this many workgroups runs in work-list mode: most of such a
+// grid would be partitions past short contexts, each costing a dispatch and a
+// load only to exit.
+constexpr int64_t kGridLimit = 16384;
+// Workgroups (over all KV heads) that walk the work list.
+constexpr int64_t kListWorkgroups = 4096;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 int32_t round_up16(int64_t x) { return (int32_t)((x + kBlock - 1) / kBlock * kBlock); }
 
-// Partition length when the caller leaves the choice to the library. Short
-// contexts run in one pass (no workspace, no merge kernel); longer ones are cut
-// into 512-token partitions, which keeps every workgroup's wave busy with 8
-// blocks while giving long sequences enough workgroups to fill 256 CUs.
+// Partition length when the caller leaves the choice to the library: the
+// longest of 4096 / 2048 / 1024 / 512 / 256 tokens whose (sequence, KV head,
+// partition) grid still has at least kMinWorkgroups workgroups (4 per CU),
+// capped by the longest context; 256 tokens when none has. Long partitions
+// mean fewer partial states to merge; the floor keeps all CUs streaming.
+// (Measured on MI355X: 256-token single pass for 60 x 8 short contexts,
+// 2048 single pass for 256 x 4 contexts of <= 2048, 4096 for 32 x 8 x 32768
+// and for skewed batches.)
+constexpr int64_t kMinWorkgroups = 1024;
+
 int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  if (max_context_len <= 512) return max_context_len <= 0 ? kBlock : round_up16(max_context_len);
-  return 512;
+  if (max_context_len <= 0) return kBlock;
+  const int32_t cap = round_up16(max_context_len);
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  for (int32_t p = kMaxPartition; p >= 256; p /= 2) {
+    const int64_t parts = ((int64_t)max_context_len + p - 1) / p;
+    if (units * parts >= kMinWorkgroups) return p < cap ? p : cap;
+  }
+  return cap < 256 ? cap : 256;
 }
+
+// Waves per workgroup: 8 for the longest partitions (more bytes in flight per
+// workgroup), else 4.
+int32_t default_waves(int32_t partition_tokens) { return partition_tokens >= 4096 ? 8 : 4; }
 
 struct Plan {
   int32_t partition_tokens;
   int32_t num_parts;
-  size_t workspace_bytes;
+  int32_t waves;
+  bool work_list;
+  int32_t list_workgroups;
+  size_t partial_bytes;    // partial (m, l, o) states, at the start of the workspace
+  size_t workspace_bytes;  // partial states + work list
 };
 
 int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -44,14 +75,31 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
       (partition_tokens < kBlock || partition_tokens > kMaxPartition || partition_tokens % kBlock))
     return MVK_ERR_INVALID_ARGUMENT;
   if (!mvk::decode_supported(head_dim, num_q_heads / num_kv_heads)) return MVK_ERR_UNSUPPORTED;
-  const int32_t p = partition_tokens ? partition_tokens
-                                     : default_partition(num_seqs, num_kv_heads, max_context_len);
+  int32_t p = partition_tokens ? partition_tokens
+                               : default_partition(num_seqs, num_kv_heads, max_context_len);
+  int32_t waves = default_waves(p);
+#ifdef MVK_TUNING
+  if (!partition_tokens && getenv("MVK_TUNE_P")) p = atoi(getenv("MVK_TUNE_P"));
+  if (getenv("MVK_TUNE_W")) waves = atoi(getenv("MVK_TUNE_W"));
+  if (p < kBlock || p > kMaxPartition || p % kBlock ||
+      (waves != 4 && waves != 8 && !(waves == 16 && num_q_heads / num_kv_heads <= 2)))
+    return MVK_ERR_INVALID_ARGUMENT;
+#endif
   int64_t parts = ((int64_t)max_context_len + p - 1) / p;
   if (parts < 1) parts = 1;
+  if (parts > kMaxGridYZ) return MVK_ERR_INVALID_ARGUMENT;  // grid z
   plan->partition_tokens = p;
   plan->num_parts = (int32_t)parts;
-  plan->workspace_bytes =
+  plan->waves = waves;
+  plan->partial_bytes =
       parts > 1 ? (size_t)num_seqs * num_q_heads * (size_t)parts * (size_t)(head_dim + 2) * 4u : 0;
+  const int64_t dense = (int64_t)num_seqs * parts * num_kv_heads;
+  plan->work_list = parts > 1 && dense > kGridLimit;
+  if (!plan->work_list && dense > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
+  const int64_t per_head = (kListWorkgroups + num_kv_heads - 1) / num_kv_heads;
+  plan->list_workgroups = (int32_t)(per_head < num_seqs * parts ? per_head : num_seqs * parts);
+  plan->workspace_bytes =
+      plan->partial_bytes + (plan->work_list ? (size_t)(1 + 2 * num_seqs * parts) * 4u : 0);
   return MVK_OK;
 }
 
@@ -147,8 +195,10 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, const void* k_cache
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   const size_t n_state = (size_t)num_seqs * num_q_heads * (size_t)plan.num_parts;
-  a.ws_ml = plan.workspace_bytes ? (float*)workspace : nullptr;
-  a.ws_o = plan.workspace_bytes ? (float*)workspace + n_state * 2 : nullptr;
+  a.ws_ml = plan.partial_bytes ? (float*)workspace : nullptr;
+  a.ws_o = plan.partial_bytes ? (float*)workspace + n_state * 2 : nullptr;
+  a.items = plan.work_list ? (int32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
+  a.list_workgroups = plan.list_workgroups;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -158,6 +208,7 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, const void* k_cache
   a.max_context_len = max_context_len;
   a.partition_tokens = plan.partition_tokens;
   a.num_parts = plan.num_parts;
+  a.waves = plan.waves;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;
   hipError_t err = mvk::launch_paged_decode(a, (hipStream_t)stream);

@@ -49,6 +49,25 @@ template <> struct Elem<1> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resource over [base, base + num_bytes): loads through it take a
+// scalar descriptor plus a 32-bit per-lane byte offset, and every byte at or
+// past num_bytes reads as zero. Word 3 selects 32-bit data format, which raw
+// (untyped) loads require to be non-zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                           kBufferWord3);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+
 // Cross-lane moves inside a 16-lane DPP row.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {

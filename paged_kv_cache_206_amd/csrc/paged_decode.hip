@@ -9,128 +9,264 @@
 // Work decomposition: one workgroup per (partition, KV head, sequence). It
 // serves all g = Hq/Hkv query heads of the GQA group, so each K/V row fetched
 // from HBM is used g times. The partition's blocks are dealt round-robin to
-// the workgroup's waves.
+// the W waves of the workgroup; every wave first fetches all of its block-table
+// entries with one vector load (issued together with the context-length load),
+// then streams its blocks with the next block's K/V loads in flight while the
+// current block is computed.
 //
-// Lane layout inside a wave (16-byte loads, one token row = D*2 bytes):
-//   LPR = D/8 lanes cover one token row (8 for D=64, 16 for D=128),
-//   RG  = 64/LPR token rows per wave-wide load, TPL = 16/RG loads per block.
-// Lane (rg, c) reads chunk c (8 elements) of token rows rg, rg+RG, ... of each
-// block, for K and for V: every load instruction reads whole rows, fully
-// coalesced. QK partial dots use v_dot2 (two fp16/bf16 products accumulated
-// in float32) and are summed over the LPR lanes of a row with DPP.
+// Per-block compute, two policies:
+//  * MFMA (g >= 4): logits as S^T = K Q^T with v_mfma_f32_16x16x32 (16 tokens x
+//    16 head slots, zero-padded past g), whose result layout (lane l holds
+//    tokens 4*(l/16)+i of head l%16) is exactly the A-operand layout of the PV
+//    product O += P V with v_mfma_f32_16x16x16. V rows are loaded coalesced
+//    (four full rows per instruction) and transposed into token pairs with
+//    v_perm_b32. P is rounded to the storage type for the PV product; the
+//    denominator sums the same rounded values.
+//  * VALU (g <= 2): lanes (rg, c) read 16-byte chunk c of token rows; v_dot2
+//    partial dots are summed over the row with DPP; PV accumulates in float32.
 //
-// Softmax: online normaliser (Milakov & Gimelshein 2018) kept per row group,
-// in base-2 units (logit * scale * log2 e). The running reference max is only
-// moved when a logit exceeds it by more than kLazyRescale, so rescaling of
-// the accumulators is rare; out = acc / l is exact for any reference.
-// Partial states of the row groups, then of the waves, then of the
-// partitions are merged with the log-sum-exp rule (FlashAttention, Dao et
-// al. 2022): M = max m_i, l = sum l_i 2^(m_i - M), o = sum o_i 2^(m_i - M) / l.
-// Merges run in a fixed order, so results are bitwise reproducible.
+// Softmax: online normaliser (Milakov & Gimelshein 2018) in base-2 units
+// (logit * scale * log2 e). The running reference max moves only when a logit
+// exceeds it by more than kLazyRescale, so accumulator rescaling is rare;
+// out = acc / l is exact for any reference. Partial states (per lane group,
+// per wave, per partition) are merged with the log-sum-exp rule
+// (FlashAttention, Dao et al. 2022): M = max m_i, l = sum l_i 2^(m_i - M),
+// o = sum o_i 2^(m_i - M) / l, always in a fixed order, so results are
+// bitwise reproducible.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace mvk {
 
-constexpr int kWaves = 4;               // waves per workgroup
-constexpr float kNegBig = -1.0e30f;     // "no token seen yet" (finite, so 2^(a-b) never sees inf-inf)
-constexpr float kLazyRescale = 8.0f;    // let p = 2^(z - m) grow up to 2^8 before rescaling
+constexpr uint32_t kXcds = 8;          // accelerator complex dies of an MI355X
+constexpr float kNegBig = -1.0e30f;   // "no token seen yet" (finite: 2^(a-b) never sees inf-inf)
+constexpr float kLazyRescale = 8.0f;  // p = 2^(z - m) may grow up to 2^8 before rescaling
 
-template <int DT, int D, int G>
-__global__ __launch_bounds__(kWaves * 64) void paged_decode_partition_kernel(
-    uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, int32_t num_kv_heads, int32_t num_blocks,
-    int32_t max_blocks, int32_t max_context_len, int32_t partition_tokens, int32_t num_parts,
-    float scale_log2) {
-  using E = Elem<DT>;
-  constexpr int LPR = D / 8;
-  constexpr int RG = 64 / LPR;
-  constexpr int TPL = kBlockTokens / RG;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-  __shared__ float sm_acc[kWaves][G][D];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int rg = lane / LPR;
-  const int c = lane % LPR;
-
-  // lengths past the host-side bound are clamped: the table row, the grid and
-  // the workspace are all sized from max_context_len (<= max_blocks * 16)
-  const int L = min(context_lens[s], max_context_len);
-  const int t_begin = part * partition_tokens;
-  if (t_begin >= L) {  // whole workgroup leaves together, before any barrier
-    if (part == 0) {   // empty context: the row is defined as zeros
-      const size_t row0 = ((size_t)s * num_kv_heads * G + (size_t)h * G) * D;
-      for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) out[row0 + idx] = 0;
-    }
-    return;
+template <int DT> struct Mma;
+template <> struct Mma<0> {  // binary16
+  static __device__ __forceinline__ f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }
-  const int t_end = min(t_begin + partition_tokens, L);
-  const int b_begin = t_begin / kBlockTokens;
-  const int b_end = (t_end + kBlockTokens - 1) / kBlockTokens;
+  static __device__ __forceinline__ f32x4_t pv(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<1> {  // bfloat16
+  static __device__ __forceinline__ f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  }
+};
 
-  const int Hq = num_kv_heads * G;
-  const size_t row_stride = (size_t)num_kv_heads * D;  // elements between token rows
-  const uint16_t* kbase = k_cache + (size_t)h * D + c * 8;
-  const uint16_t* vbase = v_cache + (size_t)h * D + c * 8;
-  const int32_t* table = block_tables + (size_t)s * max_blocks;
+// Byte selectors for v_perm_b32(hi_src, lo_src, sel): gather the low (resp.
+// high) 16-bit halves of lo_src and hi_src into one word, lo_src's first.
+constexpr uint32_t kPermLoHalves = 0x05040100u;
+constexpr uint32_t kPermHiHalves = 0x07060302u;
+
+struct Shape {
+  int32_t num_kv_heads, num_blocks, max_blocks, max_context_len, partition_tokens, num_parts;
+  float scale_log2;
+};
+
+// ------------------------------------------------------------ MFMA policy
+template <int DT, int D, int G>
+struct MfmaPolicy {
+  static_assert(G >= 1 && G <= 16, "one 16-row tile holds the whole group");
+  static constexpr int NKS = D / 32;  // QK k-steps of 32
+  static constexpr int VW = D / 16;   // V elements per lane per token row (8 or 4)
+  static constexpr int NE = VW;       // PV products (16 output columns each)
+  using VT = typename std::conditional<D == 128, uint4, uint2>::type;
+
+  struct Frag {
+    uint4 k[NKS];  // K[token l%16][32*ks + 8*(l/16) .. +7]
+    VT v[4];       // V[token 4*(l/16)+i][VW*(l%16) .. +VW-1]
+  };
+
+  uint4 qop[NKS];
+  f32x4_t acc[NE];
+  float m, lsum;
+  int r16, q4;
+  uint32_t koff, voff;  // per-lane byte offsets inside a block (loop invariant)
+
+  __device__ __forceinline__ void init(const uint16_t* q, size_t q_row0, int lane,
+                                       uint32_t row_bytes) {
+    r16 = lane & 15;
+    q4 = lane >> 4;
+    koff = r16 * row_bytes + 16u * q4;
+    voff = 4u * q4 * row_bytes + 2u * VW * r16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qop[ks] = r16 < G ? *(const uint4*)(q + (q_row0 + r16) * D + 32 * ks + 8 * q4)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = kNegBig;
+    lsum = 0.0f;
+  }
+
+  // kb/vb: wave-uniform address of this KV head's part of token 0 of the
+  // block; every lane adds its fixed offset (scalar base + vector offset)
+  // kr/vr: this KV head's slice of one block; rows past the context read as 0
+  __device__ __forceinline__ void load(Frag& f, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                       uint32_t row_bytes) const {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) f.k[ks] = buffer_load16(kr, koff + 64u * ks);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (D == 128) f.v[i] = buffer_load16(vr, voff + i * row_bytes);
+      else f.v[i] = buffer_load8(vr, voff + i * row_bytes);
+    }
+  }
+
+  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2) {
+    using M = Mma<DT>;
+    using E = Elem<DT>;
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) sc = M::qk(f.k[ks], qop[ks], sc);
+
+    const int tb = tok0 + 4 * q4;  // this lane's tokens: tb + i, head r16
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = (r16 < G && tb + i < t_end) ? sc[i] * scale_log2 : -INFINITY;
+
+    const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    if (__any(mx > m + kLazyRescale)) {
+      // new reference for every head whose block max passed the threshold;
+      // the 4 lanes of a head (l, l^16, l^32, l^48) agree on it
+      float bm = fmaxf(mx, __shfl_xor(mx, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mnew = bm > m + kLazyRescale ? bm : m;
+      const float alpha = fast_exp2(m - mnew);
+      lsum *= alpha;
+      m = mnew;
+      // acc element i holds head 4*q4+i, whose factor lives in lane 4*q4+i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e][i] *= a;
+      }
+    }
+    uint32_t pw[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint16_t p0 = E::round(fast_exp2(z[2 * i] - m));
+      const uint16_t p1 = E::round(fast_exp2(z[2 * i + 1] - m));
+      pw[i] = (uint32_t)p0 | ((uint32_t)p1 << 16);
+      lsum += E::lo(pw[i]) + E::hi(pw[i]);
+    }
+    const uint2 pa = make_uint2(pw[0], pw[1]);
+
+    const uint32_t* w0 = (const uint32_t*)&f.v[0];
+    const uint32_t* w1 = (const uint32_t*)&f.v[1];
+    const uint32_t* w2 = (const uint32_t*)&f.v[2];
+    const uint32_t* w3 = (const uint32_t*)&f.v[3];
+#pragma unroll
+    for (int k = 0; k < VW / 2; ++k) {
+      const uint2 blo = make_uint2(__builtin_amdgcn_perm(w1[k], w0[k], kPermLoHalves),
+                                   __builtin_amdgcn_perm(w3[k], w2[k], kPermLoHalves));
+      const uint2 bhi = make_uint2(__builtin_amdgcn_perm(w1[k], w0[k], kPermHiHalves),
+                                   __builtin_amdgcn_perm(w3[k], w2[k], kPermHiHalves));
+      acc[2 * k] = M::pv(pa, blo, acc[2 * k]);
+      acc[2 * k + 1] = M::pv(pa, bhi, acc[2 * k + 1]);
+    }
+  }
+
+  // Hand the wave's state to LDS: m/l per head, unnormalised o per head.
+  __device__ __forceinline__ void to_lds(float* sm_m, float* sm_l, float* sm_o) {
+    float l = lsum + __shfl_xor(lsum, 16);
+    l += __shfl_xor(l, 32);
+    if (q4 == 0 && r16 < G) {
+      sm_m[r16] = m;
+      sm_l[r16] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = 4 * q4 + i;
+      if (head < G) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) sm_o[head * D + VW * r16 + e] = acc[e][i];
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------ VALU policy
+template <int DT, int D, int G>
+struct ValuPolicy {
+  static constexpr int LPR = D / 8;              // lanes per token row (16-byte chunks)
+  static constexpr int RG = 64 / LPR;            // token rows per wave-wide load
+  static constexpr int TPL = kBlockTokens / RG;  // loads per block
+
+  struct Frag {
+    uint4 k[TPL];
+    uint4 v[TPL];
+  };
 
   uint4 qv[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j)
-    qv[j] = *(const uint4*)(q + ((size_t)s * Hq + (size_t)h * G + j) * D + c * 8);
-
   float m[G], l[G], acc[G][8];
+  int rg, c;
+  uint32_t off;  // per-lane byte offset inside a block (loop invariant)
+
+  __device__ __forceinline__ void init(const uint16_t* q, size_t q_row0, int lane,
+                                       uint32_t row_bytes) {
+    rg = lane / LPR;
+    c = lane % LPR;
+    off = rg * row_bytes + 16u * c;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = kNegBig;
-    l[j] = 0.0f;
+    for (int j = 0; j < G; ++j) qv[j] = *(const uint4*)(q + (q_row0 + j) * D + c * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+    for (int j = 0; j < G; ++j) {
+      m[j] = kNegBig;
+      l[j] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+    }
   }
 
-  for (int b = b_begin + wave; b < b_end; b += kWaves) {
-    int blk = table[b];
-    blk = ((unsigned)blk < (unsigned)num_blocks) ? blk : 0;
-    uint4 kv[TPL], vv[TPL];
+  __device__ __forceinline__ void load(Frag& f, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                       uint32_t row_bytes) const {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-      const size_t row = (size_t)blk * kBlockTokens + i * RG + rg;
-      kv[i] = *(const uint4*)(kbase + row * row_stride);
-      vv[i] = *(const uint4*)(vbase + row * row_stride);
+      const uint32_t o = off + i * RG * row_bytes;
+      f.k[i] = buffer_load16(kr, o);
+      f.v[i] = buffer_load16(vr, o);
     }
-    const int tok0 = b * kBlockTokens + rg;  // token of load i is tok0 + i*RG
-    const bool partial_block = (b + 1) * kBlockTokens > t_end;
-    if (partial_block) {
-      // rows past the context may hold anything (NaN included): zero the V
-      // words so that 0 * garbage never reaches the accumulators
-#pragma unroll
-      for (int i = 0; i < TPL; ++i)
-        if (tok0 + i * RG >= t_end) vv[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
+  }
 
+  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2) {
+    using E = Elem<DT>;
+    const int tb = tok0 + rg;  // token of load i is tb + i*RG
     float z[G][TPL];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-      const bool valid = tok0 + i * RG < t_end;
+      const bool valid = tb + i * RG < t_end;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        float d = E::dot2(qv[j].x, kv[i].x, 0.0f);
-        d = E::dot2(qv[j].y, kv[i].y, d);
-        d = E::dot2(qv[j].z, kv[i].z, d);
-        d = E::dot2(qv[j].w, kv[i].w, d);
+        float d = E::dot2(qv[j].x, f.k[i].x, 0.0f);
+        d = E::dot2(qv[j].y, f.k[i].y, d);
+        d = E::dot2(qv[j].z, f.k[i].z, d);
+        d = E::dot2(qv[j].w, f.k[i].w, d);
         d = group_sum<LPR>(d);
         z[j][i] = valid ? d * scale_log2 : -INFINITY;
       }
     }
-
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       float mx = z[j][0];
@@ -147,7 +283,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_partition_kernel(
       for (int i = 0; i < TPL; ++i) {
         const float p = fast_exp2(z[j][i] - m[j]);
         l[j] += p;
-        const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+        const uint32_t w[4] = {f.v[i].x, f.v[i].y, f.v[i].z, f.v[i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc[j][2 * e] = fmaf(p, E::lo(w[e]), acc[j][2 * e]);
@@ -157,57 +293,139 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_partition_kernel(
     }
   }
 
-  // Merge the RG row groups of this wave (lanes c, c+LPR, ... hold the same
-  // output chunk for different tokens).
+  __device__ __forceinline__ void to_lds(float* sm_m, float* sm_l, float* sm_o) {
+    // merge the RG row groups (lanes c, c+LPR, ... hold the same output chunk)
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
+    for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mo = __shfl_xor(m[j], off);
-      const float lo = __shfl_xor(l[j], off);
-      const float mm = fmaxf(m[j], mo);
-      const float a = fast_exp2(m[j] - mm);
-      const float bb = fast_exp2(mo - mm);
-      l[j] = l[j] * a + lo * bb;
+      for (int j = 0; j < G; ++j) {
+        const float mo = __shfl_xor(m[j], off);
+        const float lo = __shfl_xor(l[j], off);
+        const float mm = fmaxf(m[j], mo);
+        const float a = fast_exp2(m[j] - mm);
+        const float b = fast_exp2(mo - mm);
+        l[j] = l[j] * a + lo * b;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] = acc[j][e] * a + __shfl_xor(acc[j][e], off) * bb;
-      m[j] = mm;
+        for (int e = 0; e < 8; ++e) acc[j][e] = acc[j][e] * a + __shfl_xor(acc[j][e], off) * b;
+        m[j] = mm;
+      }
     }
-  }
-  if (rg == 0) {
+    if (rg == 0) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
+      for (int j = 0; j < G; ++j) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[wave][j][c * 8 + e] = acc[j][e];
-      if (c == 0) {
-        sm_m[wave][j] = m[j];
-        sm_l[wave][j] = l[j];
+        for (int e = 0; e < 8; ++e) sm_o[j * D + c * 8 + e] = acc[j][e];
+        if (c == 0) {
+          sm_m[j] = m[j];
+          sm_l[j] = l[j];
+        }
       }
     }
   }
+};
+
+// ------------------------------------------------------------ one work item
+// Attention of sequence s, KV head h over partition `part` (tokens
+// [part*P, min((part+1)*P, L))): the final row if the context fits in one
+// partition, else this partition's partial state. Every wave of the workgroup
+// calls it with the same arguments (it contains a barrier).
+template <int DT, int D, int G, int W, bool USE_MFMA>
+__device__ __forceinline__ void decode_item(
+    int s, int h, int part, uint16_t* __restrict__ out, float* __restrict__ ws_ml,
+    float* __restrict__ ws_o, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const Shape& sh, float (*sm_o)[G * D],
+    float (*sm_m)[G], float (*sm_l)[G]) {
+  using Policy = typename std::conditional<USE_MFMA, MfmaPolicy<DT, D, G>, ValuPolicy<DT, D, G>>::type;
+  using E = Elem<DT>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int P = sh.partition_tokens;
+  const int t_begin = part * P;
+  const int b_begin = t_begin / kBlockTokens;
+
+  // This wave's table entries (lane k <- block b_begin + wave + k*W), fetched
+  // together with the context length; the row is read only below max_blocks,
+  // and entries past the context are never used.
+  const int part_blocks = min(P / kBlockTokens, sh.max_blocks - b_begin);
+  const int32_t* table = block_tables + (size_t)s * sh.max_blocks;
+  int ent = 0;
+  if (wave + lane * W < part_blocks) ent = table[b_begin + wave + lane * W];
+
+  const int L = min(context_lens[s], sh.max_context_len);
+  const int Hq = sh.num_kv_heads * G;
+  if (t_begin >= L) {  // uniform over the workgroup
+    if (part == 0) {   // empty context: the row is defined as zeros
+      const size_t row0 = ((size_t)s * Hq + (size_t)h * G) * D;
+      for (int idx = threadIdx.x; idx < G * D; idx += W * 64) out[row0 + idx] = 0;
+    }
+    return;
+  }
+  const int t_end = min(t_begin + P, L);
+  const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
+  const int my_blocks = nblk > wave ? (nblk - wave + W - 1) / W : 0;
+
+  const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;  // one token row of the pool
+  const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
+  Policy pol;
+  pol.init(q, (size_t)s * Hq + (size_t)h * G, lane, row_bytes);
+
+  const char* kbase = (const char*)(k_cache + (size_t)h * D);
+  const char* vbase = (const char*)(v_cache + (size_t)h * D);
+  if (my_blocks > 0) {
+    // Two fragments in ping-pong: the next block's loads go out before the
+    // current block is computed, and no register copy of in-flight data is
+    // ever needed. Each block is read through a buffer descriptor covering
+    // only its rows that hold context tokens, so rows past the context (any
+    // bits, NaN included) read as zeros. The step after the last block issues
+    // its loads through an empty descriptor: they return zeros without
+    // touching memory, which keeps the load count of every step the same.
+    typename Policy::Frag fa, fb;
+    auto tok_of = [&](int k) { return (b_begin + wave + k * W) * kBlockTokens; };
+    auto load_block = [&](typename Policy::Frag& f, int k) {
+      const bool real = k < my_blocks;
+      k = min(k, my_blocks - 1);
+      int blk = __builtin_amdgcn_readlane(ent, k);
+      blk = ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
+      const int rows = min(kBlockTokens, t_end - tok_of(k));
+      const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
+      const size_t o = (size_t)blk * block_bytes;
+      pol.load(f, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
+    };
+    load_block(fa, 0);
+    for (int k = 0;;) {
+      load_block(fb, k + 1);
+      pol.process(fa, tok_of(k), t_end, sh.scale_log2);
+      if (++k >= my_blocks) break;
+      load_block(fa, k + 1);
+      pol.process(fb, tok_of(k), t_end, sh.scale_log2);
+      if (++k >= my_blocks) break;
+    }
+  }
+  pol.to_lds(sm_m[wave], sm_l[wave], sm_o[wave]);
   __syncthreads();
 
   // Merge the waves; write the final row, or this partition's partial state.
-  const int parts_of_seq = (L + partition_tokens - 1) / partition_tokens;
-  for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
+  const int parts_of_seq = (L + P - 1) / P;
+  for (int idx = threadIdx.x; idx < G * D; idx += W * 64) {
     const int j = idx / D;
     const int d = idx % D;
     float mm = sm_m[0][j];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][j]);
+    for (int w = 1; w < W; ++w) mm = fmaxf(mm, sm_m[w][j]);
     float lsum = 0.0f, o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float f = fast_exp2(sm_m[w][j] - mm);
       lsum = fmaf(sm_l[w][j], f, lsum);
-      o = fmaf(sm_acc[w][j][d], f, o);
+      o = fmaf(sm_o[w][idx], f, o);
     }
     const float r = lsum > 0.0f ? o / lsum : 0.0f;
     const size_t hq = (size_t)s * Hq + (size_t)h * G + j;
     if (parts_of_seq == 1) {
       out[hq * D + d] = E::round(r);
     } else {
-      const size_t slot = hq * num_parts + part;
+      const size_t slot = hq * sh.num_parts + part;
       ws_o[slot * D + d] = r;
       if (d == 0) {
         ws_ml[slot * 2] = mm;
@@ -217,61 +435,213 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_partition_kernel(
   }
 }
 
-// Merge the partitions of every (sequence, query head) whose context spans
-// more than one partition. One thread per output element; partitions are
-// combined in index order.
-template <int DT, int D>
-__global__ __launch_bounds__(256) void paged_decode_merge_kernel(
+// ------------------------------------------------------------ the kernel
+// Grid mode (items == nullptr): grid (S, Hkv, num_parts), one item per
+// workgroup; workgroups whose partition starts past their context exit.
+// Work-list mode: grid (X, Hkv); the plan kernel has written the count and
+// the (sequence, partition) items of all non-empty partitions, and workgroup
+// x takes items x, x+X, ... so no workgroup is launched for nothing.
+template <int DT, int D, int G, int W, bool USE_MFMA>
+__global__ __launch_bounds__(W * 64) void paged_decode_partition_kernel(
+    uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ items, Shape sh) {
+  __shared__ float sm_o[W][G * D];
+  __shared__ float sm_m[W][G];
+  __shared__ float sm_l[W][G];
+  if (items == nullptr) {
+    // Workgroups are dealt round-robin to the 8 XCDs in dispatch order; remap
+    // so that each XCD runs a contiguous range of (sequence fastest, then KV
+    // head, then partition) items. Sequences that share prefix blocks then
+    // read them on the same XCD at about the same time, from its L2.
+    const uint32_t n = gridDim.x * gridDim.y * gridDim.z;
+    const uint32_t i = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t xcd = i % kXcds, per = n / kXcds, rem = n % kXcds;
+    const uint32_t v = xcd * per + min(xcd, rem) + i / kXcds;
+    const int s = v % gridDim.x;
+    const int h = (v / gridDim.x) % gridDim.y;
+    const int part = v / (gridDim.x * gridDim.y);
+    decode_item<DT, D, G, W, USE_MFMA>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
+                                        block_tables, context_lens, sh, sm_o, sm_m, sm_l);
+    return;
+  }
+  const int count = items[0];
+  for (int i = blockIdx.x; i < count; i += gridDim.x) {
+    const int s = items[1 + 2 * i];
+    const int part = items[2 + 2 * i];
+    decode_item<DT, D, G, W, USE_MFMA>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache, v_cache,
+                                        block_tables, context_lens, sh, sm_o, sm_m, sm_l);
+    __syncthreads();  // the LDS of this item is read before the next item writes it
+  }
+}
+
+// Work list for work-list mode: items[0] = count, then (sequence, partition)
+// pairs in sequence order, one per partition that holds context tokens (one
+// partition for an empty context, which writes its zero row). One workgroup
+// of kPlanThreads threads: each thread counts a contiguous range of
+// sequences, a workgroup-wide exclusive scan gives every thread its output
+// offset, then each thread writes its own items.
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void paged_decode_plan_kernel(
+    int32_t* __restrict__ items, const int32_t* __restrict__ context_lens, int32_t num_seqs,
+    int32_t max_context_len, int32_t partition_tokens) {
+  __shared__ int32_t sums[kPlanThreads];
+  const int t = threadIdx.x;
+  const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(t * per, num_seqs);
+  const int s1 = min(s0 + per, num_seqs);
+  int n = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int L = min(context_lens[s], max_context_len);
+    n += L > 0 ? (L + partition_tokens - 1) / partition_tokens : 1;
+  }
+  sums[t] = n;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the per-thread counts
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int v = t >= off ? sums[t - off] : 0;
+    __syncthreads();
+    sums[t] += v;
+    __syncthreads();
+  }
+  int pos = sums[t] - n;
+  for (int s = s0; s < s1; ++s) {
+    const int L = min(context_lens[s], max_context_len);
+    const int parts = L > 0 ? (L + partition_tokens - 1) / partition_tokens : 1;
+    for (int p = 0; p < parts; ++p, ++pos) {
+      items[1 + 2 * pos] = s;
+      items[2 + 2 * pos] = p;
+    }
+  }
+  if (t == kPlanThreads - 1) items[0] = sums[t];
+}
+
+// Merge the partitions of every (sequence, KV head) whose context spans more
+// than one partition, for the g query heads of the group. Phase 1: the
+// per-partition weights w_p = l_p 2^(m_p - M) and their sum, one thread per
+// (head, partition), into LDS. Phase 2: one thread per (head, d) accumulates
+// sum_p w_p o_p[d] in partition order, with independent loads in flight.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxParts = 512;  // partitions merged per pass through LDS
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
-    const int32_t* __restrict__ context_lens, int32_t num_q_heads, int32_t max_context_len,
+    const int32_t* __restrict__ context_lens, int32_t num_kv_heads, int32_t max_context_len,
     int32_t partition_tokens, int32_t num_parts) {
   using E = Elem<DT>;
+  __shared__ float sm_w[G][kMergeMaxParts];
+  __shared__ float sm_max[G];
   const int s = blockIdx.y;
+  const int h = blockIdx.x;
   const int L = min(context_lens[s], max_context_len);
   const int parts = (L + partition_tokens - 1) / partition_tokens;
   if (parts <= 1) return;  // written directly by the partition kernel
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= num_q_heads * D) return;
-  const int j = idx / D;
-  const int d = idx % D;
-  const size_t hq = (size_t)s * num_q_heads + j;
-  const float* ml = ws_ml + hq * num_parts * 2;
-  const float* o = ws_o + hq * num_parts * D + d;
-  float mm = ml[0];
-  for (int p = 1; p < parts; ++p) mm = fmaxf(mm, ml[2 * p]);
-  float lsum = 0.0f, acc = 0.0f;
-  for (int p = 0; p < parts; ++p) {
-    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - mm);
-    lsum += w;
-    acc = fmaf(w, o[(size_t)p * D], acc);
+  const int Hq = num_kv_heads * G;
+  const size_t hq0 = (size_t)s * Hq + (size_t)h * G;
+  const int t = threadIdx.x;
+
+  constexpr int R = (G * D + kMergeThreads - 1) / kMergeThreads;  // outputs per thread
+  float acc[R], tot[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = tot[r] = 0.0f;
+
+  // max over the partitions of each head: one wave per head, lanes over p
+  for (int j = t / 64; j < G; j += kMergeThreads / 64) {
+    const int lane = t % 64;
+    const float* ml = ws_ml + (hq0 + j) * num_parts * 2;
+    float mm = -INFINITY;
+    for (int p = lane; p < parts; p += 64) mm = fmaxf(mm, ml[2 * p]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+    if (lane == 0) sm_max[j] = mm;
   }
-  out[hq * D + d] = E::round(lsum > 0.0f ? acc / lsum : 0.0f);
+  __syncthreads();
+  for (int p0 = 0; p0 < parts; p0 += kMergeMaxParts) {
+    const int np = min(kMergeMaxParts, parts - p0);
+    for (int idx = t; idx < G * np; idx += kMergeThreads) {
+      const int j = idx / np, p = p0 + idx % np;
+      const float* ml = ws_ml + ((hq0 + j) * num_parts + p) * 2;
+      sm_w[j][p - p0] = ml[1] * fast_exp2(ml[0] - sm_max[j]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = t + r * kMergeThreads;
+      if (idx < G * D) {
+        const int j = idx / D, d = idx % D;
+        const float* o = ws_o + ((hq0 + j) * num_parts + p0) * D + d;
+        float a = acc[r], tw = tot[r];
+#pragma unroll 8
+        for (int p = 0; p < np; ++p) {
+          const float w = sm_w[j][p];
+          a = fmaf(w, o[(size_t)p * D], a);
+          tw += w;
+        }
+        acc[r] = a;
+        tot[r] = tw;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = t + r * kMergeThreads;
+    if (idx < G * D) {
+      const int j = idx / D, d = idx % D;
+      out[(hq0 + j) * D + d] = E::round(tot[r] > 0.0f ? acc[r] / tot[r] : 0.0f);
+    }
+  }
+}
+
+template <int DT, int D, int G, int W, bool USE_MFMA>
+static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  Shape sh{a.num_kv_heads, a.num_blocks, a.max_blocks_per_seq, a.max_context_len,
+           a.partition_tokens, a.num_parts, a.scale_log2};
+  dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_parts);
+  if (a.items != nullptr) {
+    hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.items,
+                       a.context_lens, a.num_seqs, a.max_context_len, a.partition_tokens);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    grid = dim3((unsigned)a.list_workgroups, (unsigned)a.num_kv_heads, 1u);
+  }
+  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, W, USE_MFMA>), grid, dim3(W * 64),
+                     0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
+                     a.context_lens, (const int32_t*)a.items, sh);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.num_parts <= 1) return err;
+  dim3 mgrid((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+  hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, G>), mgrid, dim3(kMergeThreads), 0, stream,
+                     (uint16_t*)a.out, a.ws_ml, a.ws_o, a.context_lens, a.num_kv_heads,
+                     a.max_context_len, a.partition_tokens, a.num_parts);
+  return hipGetLastError();
 }
 
 template <int DT, int D, int G>
-static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G>), grid, dim3(kWaves * 64), 0, stream,
-                     (uint16_t*)a.out, a.ws_ml, a.ws_o, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
-                     a.context_lens, a.num_kv_heads, a.num_blocks, a.max_blocks_per_seq,
-                     a.max_context_len, a.partition_tokens, a.num_parts, a.scale_log2);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.num_parts <= 1) return err;
-  dim3 mgrid((unsigned)((a.num_q_heads * D + 255) / 256), (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D>), mgrid, dim3(256), 0, stream,
-                     (uint16_t*)a.out, a.ws_ml, a.ws_o, a.context_lens, a.num_q_heads,
-                     a.max_context_len, a.partition_tokens, a.num_parts);
-  return hipGetLastError();
+static hipError_t launch_waves(const DecodeArgs& a, hipStream_t stream) {
+  constexpr bool kMfma = G >= 4;  // g <= 2: VALU keeps up with HBM; g >= 4: MFMA
+  switch (a.waves) {
+    case 4: return launch_typed<DT, D, G, 4, kMfma>(a, stream);
+    case 8: return launch_typed<DT, D, G, 8, kMfma>(a, stream);
+    case 16:
+      // 16 waves fit one CU only at <= 128 VGPRs: VALU variant only
+      if constexpr (!kMfma) return launch_typed<DT, D, G, 16, kMfma>(a, stream);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int DT, int D>
 static hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_typed<DT, D, 1>(a, stream);
-    case 2: return launch_typed<DT, D, 2>(a, stream);
-    case 4: return launch_typed<DT, D, 4>(a, stream);
-    case 8: return launch_typed<DT, D, 8>(a, stream);
+    case 1: return launch_waves<DT, D, 1>(a, stream);
+    case 2: return launch_waves<DT, D, 2>(a, stream);
+    case 4: return launch_waves<DT, D, 4>(a, stream);
+    case 8: return launch_waves<DT, D, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

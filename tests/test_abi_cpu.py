@@ -62,7 +62,7 @@ def decode_call(mvk, **over):
                 part=0, ws=None, wsb=0, stream=None)
     args.update(over)
     a = args
-    return mvk._lib.mvk_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"],
+    return mvk.lib().mvk_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"],
                                                a["S"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
                                                a["mb"], a["maxlen"], a["scale"], a["dtype"],
                                                a["part"], a["ws"], a["wsb"], a["stream"])
@@ -103,7 +103,7 @@ def cache_call(mvk, **over):
     a = dict(key=FAKE, value=FAKE * 2, kc=FAKE * 3, vc=FAKE * 4, slots=FAKE * 5, T=4, hkv=2, d=64,
              bs=16, nb=32, dtype=0, stream=None)
     a.update(over)
-    return mvk._lib.mvk_reshape_and_cache(a["key"], a["value"], a["kc"], a["vc"], a["slots"],
+    return mvk.lib().mvk_reshape_and_cache(a["key"], a["value"], a["kc"], a["vc"], a["slots"],
                                           a["T"], a["hkv"], a["d"], a["bs"], a["nb"], a["dtype"],
                                           a["stream"])
 
@@ -128,5 +128,9 @@ def test_workspace_size(mvk):
     assert p == 512 and nbytes == 32 * 32 * 64 * (128 + 2) * 4
     nbytes, p = mvk.workspace_size(2, 2, 1, 64, 0)
     assert nbytes == 0
+    # skewed batch: the dense grid would be huge, so a work list is appended
+    nbytes, p = mvk.workspace_size(512, 16, 8, 128, 131072, 1024)
+    parts = 131072 // 1024
+    assert nbytes == 512 * 16 * parts * 130 * 4 + (1 + 2 * 512 * parts) * 4
     with pytest.raises(mvk.MvkError):
         mvk.workspace_size(2, 3, 2, 64, 10)

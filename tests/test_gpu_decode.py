@@ -166,3 +166,24 @@ def test_output_into_strided_batch_slice():
     torch.cuda.synchronize()
     assert torch.all(big[0] == 0) and torch.all(big[3] == 0)
     assert max_err(out, oracle_decode(wl), "bf16") <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,d,g,p", [("bf16", 128, 2, 16), ("f16", 64, 8, 32), ("bf16", 128, 4, 48)])
+def test_work_list_mode(dtype, d, g, p):
+    """Many sequences with skewed lengths (empty and one-token ones included)
+    and short partitions: the dense grid would be mostly empty, so the library
+    walks a compact work list instead."""
+    gen = torch.Generator().manual_seed(d + g)
+    lens = torch.randint(0, 700, (300,), generator=gen)
+    lens[::17] = 0
+    lens[5::23] = 1
+    lens[7] = 1500
+    hkv = 8
+    nbytes, chosen = mvk.workspace_size(300, g * hkv, hkv, d, int(lens.max()), p)
+    parts = -(-int(lens.max()) // p)
+    assert 300 * parts * hkv > 16384 and nbytes > 300 * g * hkv * parts * (d + 2) * 4
+    wl = custom(dtype, lens.tolist(), g * hkv, hkv, d, seed=13)
+    W.poison_unread(wl)
+    out, _ = parity(wl, partition_tokens=p)
+    zero_rows = out[lens == 0]
+    assert torch.all(zero_rows == 0)
