@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MVK_ABI_VERSION 1
+#define MVK_ABI_VERSION 2
 
 typedef enum mvk_status {
     MVK_OK = 0,
@@ -119,7 +119,8 @@ int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads
                                            int32_t* chosen_partition_tokens);
 
 /*
- * mvk_paged_attention_decode - one batched decode step of paged attention.
+ * mvk_paged_attention_decode - one batched decode step of paged attention,
+ * optionally with that step's cache write fused in.
  *
  * Defines, for every sequence s, query head j and d < head_dim, with
  * L = context_lens[s], g = num_q_heads / num_kv_heads and h = j / g
@@ -127,20 +128,32 @@ int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads
  *   z_t        = scale * sum_d q[s][j][d] * K_t[h][d]        for t < L,
  *   out[s][j]  = sum_t softmax(z)_t * V_t[h]
  * where K_t / V_t are token t's rows fetched through block_tables[s]. The new
- * token of this step must already be in the pools (mvk_reshape_and_cache first)
- * and counted in L. L == 0 gives an all-zero row. Arithmetic is float32
- * (products, logits, softmax, accumulation); out is rounded to nearest-even.
- * (Method: mini-vllm write-up, "2. 分页KV缓存（PagedAttention）" and
- * "关键工程决策" items 1-3; micro-vLLM wiki, paged-attention backend.)
+ * token of this step counts in L and must be in the pools when attention reads
+ * it: stored earlier with mvk_reshape_and_cache, or passed in new_key /
+ * new_value / slot_mapping (below). L == 0 gives an all-zero row. Arithmetic
+ * is float32 (products, logits, softmax, accumulation); out is rounded to
+ * nearest-even. (Method: mini-vllm write-up, "2. 分页KV缓存（PagedAttention）"
+ * and "关键工程决策" items 1-3; micro-vLLM wiki, paged-attention backend.)
  *
  *   out           [num_seqs, num_q_heads, head_dim], dtype, written.
  *   q             [num_seqs, num_q_heads, head_dim], dtype.
- *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim], dtype.
- *   v_cache
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim], dtype; read,
+ *   v_cache       and written only by the fused cache write.
  *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entries past
  *                 ceil(L / 16) are never read (any value).
  *   context_lens  int32 [num_seqs]; each must be <= max_context_len (tokens
  *                 past it are ignored).
+ *   new_key,      fused cache write, all three NULL or all three set:
+ *   new_value     [num_seqs, num_kv_heads, head_dim], dtype: row s is sequence
+ *   slot_mapping  s's token of this step; int32 [num_seqs] its flat slot
+ *                 (negative = no write). The rows are stored exactly as
+ *                 mvk_reshape_and_cache(new_key, new_value, ..., num_seqs)
+ *                 would store them (bit-exact), and sequence s's attention
+ *                 sees row s wherever its slot lies in s's own context. A slot
+ *                 that lies in another sequence's context is stored, but what
+ *                 that other sequence reads for it in the same call is
+ *                 unspecified (a paged allocator never appends into a block
+ *                 another sequence reads).
  *   max_context_len  host-side upper bound of context_lens; sizes the split.
  *                 Must be <= max_blocks_per_seq * 16.
  *   scale         finite float multiplier of the raw dot products.
@@ -155,13 +168,16 @@ int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads
  * Unused pool slots and the unread tail of a sequence's last block may hold
  * any bits, NaN included: they do not reach the output.
  * The output does not depend on the order in which the GPU runs work items:
- * repeated calls with the same inputs give identical bits.
+ * repeated calls with the same inputs give identical bits, and a fused call
+ * gives the same bits as the cache write followed by the unfused call.
  * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED,
  * MVK_ERR_WORKSPACE_TOO_SMALL, MVK_ERR_HIP.
  */
 int32_t mvk_paged_attention_decode(void* out, const void* q,
-                                   const void* k_cache, const void* v_cache,
+                                   void* k_cache, void* v_cache,
                                    const int32_t* block_tables, const int32_t* context_lens,
+                                   const void* new_key, const void* new_value,
+                                   const int32_t* slot_mapping,
                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                    int32_t max_blocks_per_seq, int32_t max_context_len,

@@ -7,7 +7,8 @@ is no fallback: if libmvk.so is missing, the first call fails with instructions.
     reshape_and_cache(key, value, k_cache, v_cache, slot_mapping)
     paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
                            max_context_len=None, out=None, partition_tokens=0,
-                           workspace=None)
+                           workspace=None, new_key=None, new_value=None,
+                           slot_mapping=None)
 
 The loader relies on torch having loaded its HIP runtime first: the library's
 dependency on libamdhip64.so.7 then resolves to that same runtime, so the
@@ -23,6 +24,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmvk.so")
 
+ABI_VERSION = 2
 MVK_OK = 0
 MVK_ERR_INVALID_ARGUMENT = 1
 MVK_ERR_UNSUPPORTED = 2
@@ -43,9 +45,10 @@ SIGNATURES = {
     "mvk_paged_attention_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                                     ctypes.POINTER(_c_size),
                                                     ctypes.POINTER(_c_int)]),
-    "mvk_paged_attention_decode": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int,
+    "mvk_paged_attention_decode": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                            _c_float, _c_int, _c_int, _ptr, _c_size, _ptr]),
+                                            _c_int, _c_int, _c_float, _c_int, _c_int, _ptr,
+                                            _c_size, _ptr]),
 }
 
 
@@ -77,8 +80,8 @@ def lib() -> ctypes.CDLL:
     global _LIB
     if _LIB is None:
         loaded = load_library()
-        if loaded.mvk_abi_version() != 1:
-            raise ImportError(f"libmvk ABI version {loaded.mvk_abi_version()} != 1")
+        if loaded.mvk_abi_version() != ABI_VERSION:
+            raise ImportError(f"libmvk ABI version {loaded.mvk_abi_version()} != {ABI_VERSION}")
         _LIB = loaded
     return _LIB
 
@@ -157,10 +160,16 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
 def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                            max_context_len: int | None = None, out: torch.Tensor | None = None,
-                           partition_tokens: int = 0,
-                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+                           partition_tokens: int = 0, workspace: torch.Tensor | None = None,
+                           new_key: torch.Tensor | None = None,
+                           new_value: torch.Tensor | None = None,
+                           slot_mapping: torch.Tensor | None = None) -> torch.Tensor:
     """One batched decode step: out[s, j] = softmax(scale * q[s, j] K_s^T) V_s
     over the context_lens[s] tokens reached through block_tables[s].
+
+    With new_key / new_value ([S, Hkv, D]) and slot_mapping (int32 [S]) the
+    step's cache write is fused in: row s is stored at slot_mapping[s] and
+    sequence s attends over it.
 
     `max_context_len` must bound context_lens; when omitted it is read from the
     device (a synchronising copy). `workspace` (uint8, on the device) is
@@ -175,6 +184,19 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     if v_cache.shape != k_cache.shape or d2 != d or block_tables.shape[0] != S \
             or context_lens.shape[0] != S:
         raise ValueError("inconsistent shapes")
+    fused = (new_key, new_value, slot_mapping)
+    if any(t is not None for t in fused):
+        if any(t is None for t in fused):
+            raise ValueError("new_key, new_value and slot_mapping go together")
+        _require(new_key, "new_key", dtype=q.dtype, ndim=3)
+        _require(new_value, "new_value", dtype=q.dtype, ndim=3)
+        _require(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+        if new_key.shape != (S, hkv, d) or new_value.shape != new_key.shape \
+                or slot_mapping.shape[0] != S:
+            raise ValueError("fused cache write: new rows must be [num_seqs, Hkv, D]")
+        nk, nv, sm = new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr()
+    else:
+        nk = nv = sm = None
     if max_context_len is None:
         max_context_len = int(context_lens.max().item()) if S else 0
     if out is None:
@@ -191,10 +213,10 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _require(workspace, "workspace", dtype=torch.uint8)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     st = lib().mvk_paged_attention_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
-                                         v_cache.data_ptr(), block_tables.data_ptr(),
-                                         context_lens.data_ptr(), S, hq, hkv, d, bs, nb,
-                                         block_tables.shape[1], max_context_len, float(scale),
-                                         _dtype_code(q), partition_tokens, ws_ptr, ws_bytes,
-                                         _stream(q.device))
+                                          v_cache.data_ptr(), block_tables.data_ptr(),
+                                          context_lens.data_ptr(), nk, nv, sm, S, hq, hkv, d, bs,
+                                          nb, block_tables.shape[1], max_context_len,
+                                          float(scale), _dtype_code(q), partition_tokens, ws_ptr,
+                                          ws_bytes, _stream(q.device))
     _check("mvk_paged_attention_decode", st)
     return out

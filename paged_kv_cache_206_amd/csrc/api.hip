@@ -157,9 +157,10 @@ int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads
   return MVK_OK;
 }
 
-int32_t mvk_paged_attention_decode(void* out, const void* q, const void* k_cache,
-                                   const void* v_cache, const int32_t* block_tables,
-                                   const int32_t* context_lens, int32_t num_seqs,
+int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const void* new_key, const void* new_value,
+                                   const int32_t* slot_mapping, int32_t num_seqs,
                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t block_size, int32_t num_blocks,
                                    int32_t max_blocks_per_seq, int32_t max_context_len,
@@ -181,7 +182,14 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, const void* k_cache
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned4(block_tables) || !aligned4(context_lens))
     return MVK_ERR_INVALID_ARGUMENT;
-  if (out == q || out == k_cache || out == v_cache) return MVK_ERR_INVALID_ARGUMENT;
+  if (out == q || out == k_cache || out == v_cache || k_cache == v_cache)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (new_key || new_value || slot_mapping) {  // fused cache write: all three or none
+    if (!new_key || !new_value || !slot_mapping) return MVK_ERR_INVALID_ARGUMENT;
+    if (!aligned16(new_key) || !aligned16(new_value) || !aligned4(slot_mapping))
+      return MVK_ERR_INVALID_ARGUMENT;
+    if ((int64_t)num_blocks * kBlock > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
+  }
   if (plan.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan.workspace_bytes) return MVK_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace)) return MVK_ERR_INVALID_ARGUMENT;
@@ -194,6 +202,9 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, const void* k_cache
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.new_key = new_key;
+  a.new_value = new_value;
+  a.slot_mapping = slot_mapping;
   const size_t n_state = (size_t)num_seqs * num_q_heads * (size_t)plan.num_parts;
   a.ws_ml = plan.partial_bytes ? (float*)workspace : nullptr;
   a.ws_o = plan.partial_bytes ? (float*)workspace + n_state * 2 : nullptr;

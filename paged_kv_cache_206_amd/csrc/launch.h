@@ -19,6 +19,9 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const void* new_key;          // fused cache write (nullptr = none): [S, Hkv, D]
+  const void* new_value;
+  const int32_t* slot_mapping;  // [S]
   float* ws_ml;  // [S, Hq, num_parts, 2] (running max in log2 units, denominator)
   float* ws_o;   // [S, Hq, num_parts, D] normalised partial outputs
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;

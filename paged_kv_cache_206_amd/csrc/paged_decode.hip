@@ -82,6 +82,14 @@ struct Shape {
   float scale_log2;
 };
 
+// Optional fused cache write: row s of key/value ([S, Hkv, D]) is sequence
+// s's token of this step, stored at flat slot slots[s] (negative = none).
+struct NewRows {
+  const uint16_t* key;
+  const uint16_t* value;
+  const int32_t* slots;
+};
+
 // ------------------------------------------------------------ MFMA policy
 template <int DT, int D, int G>
 struct MfmaPolicy {
@@ -133,7 +141,10 @@ struct MfmaPolicy {
     }
   }
 
-  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2) {
+  // `sub` (substitute a new row) is never set for this policy: fused calls
+  // with g >= 4 store the new rows with the cache-write kernel first.
+  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub) {
+    (void)sub;
     using M = Mma<DT>;
     using E = Elem<DT>;
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -223,6 +234,17 @@ struct ValuPolicy {
   float m[G], l[G], acc[G][8];
   int rg, c;
   uint32_t off;  // per-lane byte offset inside a block (loop invariant)
+  uint4 nk, nv;  // this lane's chunk of the step's new K/V row (fused cache write)
+  int row_new;   // offset of the new row inside its block
+
+  // Load chunk c of the new K/V row of this KV head; the block that holds it
+  // will take these values for that row instead of what memory holds.
+  __device__ __forceinline__ void set_new_row(const uint16_t* key_row, const uint16_t* value_row,
+                                              int row) {
+    nk = *(const uint4*)(key_row + c * 8);
+    nv = *(const uint4*)(value_row + c * 8);
+    row_new = row;
+  }
 
   __device__ __forceinline__ void init(const uint16_t* q, size_t q_row0, int lane,
                                        uint32_t row_bytes) {
@@ -250,8 +272,17 @@ struct ValuPolicy {
     }
   }
 
-  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2) {
+  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub) {
     using E = Elem<DT>;
+    if (sub) {  // this block holds the step's new row
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        if (i * RG + rg == row_new) {
+          f.k[i] = nk;
+          f.v[i] = nv;
+        }
+      }
+    }
     const int tb = tok0 + rg;  // token of load i is tb + i*RG
     float z[G][TPL];
 #pragma unroll
@@ -329,13 +360,14 @@ struct ValuPolicy {
 // [part*P, min((part+1)*P, L))): the final row if the context fits in one
 // partition, else this partition's partial state. Every wave of the workgroup
 // calls it with the same arguments (it contains a barrier).
-template <int DT, int D, int G, int W, bool USE_MFMA>
+template <int DT, int D, int G, int W, bool USE_MFMA, bool FUSED>
 __device__ __forceinline__ void decode_item(
     int s, int h, int part, uint16_t* __restrict__ out, float* __restrict__ ws_ml,
-    float* __restrict__ ws_o, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, const Shape& sh, float (*sm_o)[G * D],
-    float (*sm_m)[G], float (*sm_l)[G]) {
+    float* __restrict__ ws_o, const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const Shape& sh, const NewRows& nr,
+    float (*sm_o)[G * D], float (*sm_m)[G], float (*sm_l)[G]) {
+  static_assert(!(FUSED && USE_MFMA), "fused cache write runs with the VALU policy only");
   using Policy = typename std::conditional<USE_MFMA, MfmaPolicy<DT, D, G>, ValuPolicy<DT, D, G>>::type;
   using E = Elem<DT>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -354,6 +386,26 @@ __device__ __forceinline__ void decode_item(
 
   const int L = min(context_lens[s], sh.max_context_len);
   const int Hq = sh.num_kv_heads * G;
+  const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;  // one token row of the pool
+  int blk_new = -1, row_new = 0;
+  const uint16_t* new_k = nullptr;
+  const uint16_t* new_v = nullptr;
+  if constexpr (FUSED) {
+    const int slot = nr.slots[s];
+    if (slot >= 0 && slot < sh.num_blocks * kBlockTokens) {
+      blk_new = slot / kBlockTokens;
+      row_new = slot % kBlockTokens;
+      const size_t src = ((size_t)s * sh.num_kv_heads + h) * D;
+      new_k = nr.key + src;
+      new_v = nr.value + src;
+      // the store of record of this KV head's slice: one wave of partition 0
+      if (part == 0 && wave == 0 && lane < D / 8) {
+        const size_t dst = (size_t)slot * sh.num_kv_heads * D + (size_t)h * D + lane * 8;
+        *(uint4*)(k_cache + dst) = *(const uint4*)(new_k + lane * 8);
+        *(uint4*)(v_cache + dst) = *(const uint4*)(new_v + lane * 8);
+      }
+    }
+  }
   if (t_begin >= L) {  // uniform over the workgroup
     if (part == 0) {   // empty context: the row is defined as zeros
       const size_t row0 = ((size_t)s * Hq + (size_t)h * G) * D;
@@ -365,10 +417,12 @@ __device__ __forceinline__ void decode_item(
   const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
   const int my_blocks = nblk > wave ? (nblk - wave + W - 1) / W : 0;
 
-  const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;  // one token row of the pool
   const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
   Policy pol;
   pol.init(q, (size_t)s * Hq + (size_t)h * G, lane, row_bytes);
+  if constexpr (FUSED) {
+    if (blk_new >= 0) pol.set_new_row(new_k, new_v, row_new);
+  }
 
   const char* kbase = (const char*)(k_cache + (size_t)h * D);
   const char* vbase = (const char*)(v_cache + (size_t)h * D);
@@ -382,23 +436,27 @@ __device__ __forceinline__ void decode_item(
     // touching memory, which keeps the load count of every step the same.
     typename Policy::Frag fa, fb;
     auto tok_of = [&](int k) { return (b_begin + wave + k * W) * kBlockTokens; };
+    auto block_of = [&](int k) {
+      int blk = __builtin_amdgcn_readlane(ent, min(k, my_blocks - 1));
+      return ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
+    };
     auto load_block = [&](typename Policy::Frag& f, int k) {
       const bool real = k < my_blocks;
+      const int blk = block_of(k);
       k = min(k, my_blocks - 1);
-      int blk = __builtin_amdgcn_readlane(ent, k);
-      blk = ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
       const int rows = min(kBlockTokens, t_end - tok_of(k));
       const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
       const size_t o = (size_t)blk * block_bytes;
       pol.load(f, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
     };
+    auto is_new = [&](int k) { return FUSED && block_of(k) == blk_new; };
     load_block(fa, 0);
     for (int k = 0;;) {
       load_block(fb, k + 1);
-      pol.process(fa, tok_of(k), t_end, sh.scale_log2);
+      pol.process(fa, tok_of(k), t_end, sh.scale_log2, is_new(k));
       if (++k >= my_blocks) break;
       load_block(fa, k + 1);
-      pol.process(fb, tok_of(k), t_end, sh.scale_log2);
+      pol.process(fb, tok_of(k), t_end, sh.scale_log2, is_new(k));
       if (++k >= my_blocks) break;
     }
   }
@@ -441,12 +499,13 @@ __device__ __forceinline__ void decode_item(
 // Work-list mode: grid (X, Hkv); the plan kernel has written the count and
 // the (sequence, partition) items of all non-empty partitions, and workgroup
 // x takes items x, x+X, ... so no workgroup is launched for nothing.
-template <int DT, int D, int G, int W, bool USE_MFMA>
+template <int DT, int D, int G, int W, bool USE_MFMA, bool FUSED>
 __global__ __launch_bounds__(W * 64) void paged_decode_partition_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ items, Shape sh) {
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ items, Shape sh,
+    NewRows nr) {
   __shared__ float sm_o[W][G * D];
   __shared__ float sm_m[W][G];
   __shared__ float sm_l[W][G];
@@ -462,16 +521,18 @@ __global__ __launch_bounds__(W * 64) void paged_decode_partition_kernel(
     const int s = v % gridDim.x;
     const int h = (v / gridDim.x) % gridDim.y;
     const int part = v / (gridDim.x * gridDim.y);
-    decode_item<DT, D, G, W, USE_MFMA>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
-                                        block_tables, context_lens, sh, sm_o, sm_m, sm_l);
+    decode_item<DT, D, G, W, USE_MFMA, FUSED>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
+                                               block_tables, context_lens, sh, nr, sm_o, sm_m,
+                                               sm_l);
     return;
   }
   const int count = items[0];
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int s = items[1 + 2 * i];
     const int part = items[2 + 2 * i];
-    decode_item<DT, D, G, W, USE_MFMA>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache, v_cache,
-                                        block_tables, context_lens, sh, sm_o, sm_m, sm_l);
+    decode_item<DT, D, G, W, USE_MFMA, FUSED>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache,
+                                               v_cache, block_tables, context_lens, sh, nr, sm_o,
+                                               sm_m, sm_l);
     __syncthreads();  // the LDS of this item is read before the next item writes it
   }
 }
@@ -596,10 +657,11 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_kernel(
   }
 }
 
-template <int DT, int D, int G, int W, bool USE_MFMA>
+template <int DT, int D, int G, int W, bool USE_MFMA, bool FUSED>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   Shape sh{a.num_kv_heads, a.num_blocks, a.max_blocks_per_seq, a.max_context_len,
            a.partition_tokens, a.num_parts, a.scale_log2};
+  NewRows nr{(const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.slot_mapping};
   dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_parts);
   if (a.items != nullptr) {
     hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.items,
@@ -608,10 +670,10 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     grid = dim3((unsigned)a.list_workgroups, (unsigned)a.num_kv_heads, 1u);
   }
-  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, W, USE_MFMA>), grid, dim3(W * 64),
-                     0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
-                     a.context_lens, (const int32_t*)a.items, sh);
+  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, W, USE_MFMA, FUSED>), grid,
+                     dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
+                     (const uint16_t*)a.q, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache,
+                     a.block_tables, a.context_lens, (const int32_t*)a.items, sh, nr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_parts <= 1) return err;
   dim3 mgrid((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
@@ -624,14 +686,34 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 template <int DT, int D, int G>
 static hipError_t launch_waves(const DecodeArgs& a, hipStream_t stream) {
   constexpr bool kMfma = G >= 4;  // g <= 2: VALU keeps up with HBM; g >= 4: MFMA
-  switch (a.waves) {
-    case 4: return launch_typed<DT, D, G, 4, kMfma>(a, stream);
-    case 8: return launch_typed<DT, D, G, 8, kMfma>(a, stream);
-    case 16:
-      // 16 waves fit one CU only at <= 128 VGPRs: VALU variant only
-      if constexpr (!kMfma) return launch_typed<DT, D, G, 16, kMfma>(a, stream);
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+  if constexpr (kMfma) {
+    if (a.new_key != nullptr) {
+      // fused call with the MFMA policy: the cache-write kernel goes first on
+      // the same stream, then attention reads the stored rows
+      const int64_t row_vecs = (int64_t)a.num_kv_heads * D * 2 / 16;
+      hipError_t err = launch_cache_write(a.new_key, a.new_value, (void*)a.k_cache,
+                                          (void*)a.v_cache, a.slot_mapping, a.num_seqs,
+                                          (int32_t)row_vecs, (int64_t)a.num_blocks * kBlockTokens,
+                                          stream);
+      if (err != hipSuccess) return err;
+    }
+    switch (a.waves) {
+      case 4: return launch_typed<DT, D, G, 4, true, false>(a, stream);
+      case 8: return launch_typed<DT, D, G, 8, true, false>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    const bool fused = a.new_key != nullptr;
+    switch (a.waves) {
+      case 4: return fused ? launch_typed<DT, D, G, 4, false, true>(a, stream)
+                           : launch_typed<DT, D, G, 4, false, false>(a, stream);
+      case 8: return fused ? launch_typed<DT, D, G, 8, false, true>(a, stream)
+                           : launch_typed<DT, D, G, 8, false, false>(a, stream);
+      // 16 waves fit one CU only at <= 128 VGPRs: VALU policy only
+      case 16: return fused ? launch_typed<DT, D, G, 16, false, true>(a, stream)
+                            : launch_typed<DT, D, G, 16, false, false>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 

@@ -47,7 +47,7 @@ def test_single_hip_runtime_mapped(mvk):
 
 
 def test_version_and_status_strings(mvk):
-    assert mvk.abi_version() == 1
+    assert mvk.abi_version() == 2
     assert mvk.status_string(0) == "ok"
     assert mvk.status_string(3) == "workspace too small"
     assert mvk.status_string(99) == "unknown status"
@@ -57,15 +57,16 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 
 
 def decode_call(mvk, **over):
-    args = dict(out=FAKE, q=FAKE * 2, k=FAKE * 3, v=FAKE * 4, bt=FAKE * 5, cl=FAKE * 6, S=4,
-                hq=4, hkv=2, d=64, bs=16, nb=32, mb=4, maxlen=45, scale=0.125, dtype=0,
-                part=0, ws=None, wsb=0, stream=None)
+    args = dict(out=FAKE, q=FAKE * 2, k=FAKE * 3, v=FAKE * 4, bt=FAKE * 5, cl=FAKE * 6, nk=None,
+                nv=None, sm=None, S=4, hq=4, hkv=2, d=64, bs=16, nb=32, mb=4, maxlen=45,
+                scale=0.125, dtype=0, part=0, ws=None, wsb=0, stream=None)
     args.update(over)
     a = args
     return mvk.lib().mvk_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"],
-                                               a["S"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
-                                               a["mb"], a["maxlen"], a["scale"], a["dtype"],
-                                               a["part"], a["ws"], a["wsb"], a["stream"])
+                                                a["nk"], a["nv"], a["sm"], a["S"], a["hq"],
+                                                a["hkv"], a["d"], a["bs"], a["nb"], a["mb"],
+                                                a["maxlen"], a["scale"], a["dtype"], a["part"],
+                                                a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -88,6 +89,10 @@ def decode_call(mvk, **over):
     (dict(q=None), 1),
     (dict(out=FAKE + 2), 1),          # misaligned
     (dict(out=FAKE * 2), 1),          # out aliases q
+    (dict(v=FAKE * 3), 1),            # k_cache and v_cache must differ
+    (dict(nk=FAKE * 8), 1),           # fused write needs all three of key, value, slots
+    (dict(nk=FAKE * 8, nv=FAKE * 9), 1),
+    (dict(nk=FAKE * 8 + 4, nv=FAKE * 9, sm=FAKE * 10), 1),
     (dict(mb=64, maxlen=1024, part=512, ws=None, wsb=0), 3),
     (dict(mb=64, maxlen=1024, part=512, ws=FAKE * 7, wsb=100), 3),
 ])

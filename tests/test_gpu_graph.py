@@ -1,0 +1,70 @@
+"""Captured HIP graphs of the decode step (cache write + decode per layer)
+replay bit-identically to eager calls. Every replay is preceded by eager work
+and a synchronisation and is checked against the eager result."""
+import pytest
+import torch
+
+import paged_kv_cache_206_amd as mvk
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def run_step(wl, bt, cl, slots, outs, partition_tokens, ws, maxlen, fused=False):
+    for l, out in zip(wl.layers, outs):
+        if fused:
+            mvk.paged_attention_decode(l.q, l.k_cache, l.v_cache, bt, cl, wl.scale,
+                                       max_context_len=maxlen, out=out,
+                                       partition_tokens=partition_tokens, workspace=ws,
+                                       new_key=l.key, new_value=l.value, slot_mapping=slots)
+            continue
+        mvk.reshape_and_cache(l.key, l.value, l.k_cache, l.v_cache, slots)
+        mvk.paged_attention_decode(l.q, l.k_cache, l.v_cache, bt, cl, wl.scale,
+                                   max_context_len=maxlen, out=out,
+                                   partition_tokens=partition_tokens, workspace=ws)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_write", "fused_write"])
+@pytest.mark.parametrize("case", ["single_pass", "split_merge", "work_list"])
+def test_graph_replay_matches_eager(case, fused):
+    if case == "single_pass":
+        wl = W.make("qwen3", layers=3)
+        p = 0
+    elif case == "split_merge":
+        wl = W.make_custom("g", "bf16", [900, 17, 1, 2000, 640], 32, 8, 128, 400, 21, layers=2)
+        p = 256
+    else:
+        gen = torch.Generator().manual_seed(5)
+        lens = torch.randint(1, 400, (200,), generator=gen).tolist()
+        wl = W.make_custom("g", "f16", lens, 16, 8, 64, sum(-(-L // 16) for L in lens) + 8, 22,
+                           layers=2)
+        p = 32
+    maxlen = wl.max_context_len          # host-side, before anything is captured
+    wl = wl.to("cuda")
+    bt, cl, slots = wl.block_tables, wl.context_lens, wl.slot_mapping
+    nbytes, _ = mvk.workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                   maxlen, p)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    eager = [torch.empty_like(l.q) for l in wl.layers]
+    run_step(wl, bt, cl, slots, eager, p, ws, maxlen, fused)
+    torch.cuda.synchronize()
+
+    graphed = [torch.empty_like(l.q) for l in wl.layers]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_step(wl, bt, cl, slots, graphed, p, ws, maxlen, fused)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_step(wl, bt, cl, slots, graphed, p, ws, maxlen, fused)
+    for rep in range(3):
+        for o in graphed:
+            o.fill_(float("nan"))
+        x = torch.randn(512, 512, device="cuda")
+        (x @ x).sum().item()           # unrelated eager work, then a sync
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, graphed):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (case, rep)
