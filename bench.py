@@ -52,9 +52,12 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library choice)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, --steps times (calibrates "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     ap.add_argument("--unfused", action="store_true",
                     help="cache write as its own call instead of fused into the decode call")
     return ap.parse_args()
@@ -76,6 +79,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe(torch, dev, args.copy_probe, args.steps)
+        return
     wl = W.make(args.workload, value_device="cuda")   # seeded; values drawn on the GPU
     nsets = POOL_SETS.get(args.workload, 1)
     layers = list(wl.layers)
@@ -152,13 +158,15 @@ def main():
     timed_steps = replays * nsets
     ms_per_step = wall / timed_steps * 1e3
 
-    # ---- decode kernel alone: graph of back-to-back decode launches, one
-    # event pair on the replay stream around all replays
+    # ---- the step's decode call alone (with its fused cache write unless
+    # --unfused): graph of back-to-back calls, one event pair on the replay
+    # stream around all replays
+    fused = not args.unfused
     cur = torch.cuda.current_stream(dev)
     dgraph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(dgraph):
         for li in range(len(layers)):
-            layer_call(li, write=False)
+            layer_call(li, write=fused)
     dgraph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -169,14 +177,14 @@ def main():
     e1.record(cur)
     torch.cuda.synchronize()
     launch_us = e0.elapsed_time(e1) * 1e3 / (reps * len(layers))
-    # eager decode launches with an event pair around each one (includes the
-    # dispatch of every launch)
+    # eager calls with an event pair around each one (includes the dispatch
+    # of every launch)
     n_ev = min(args.steps * nlayers_step, 4 * len(layers))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_ev)]
     for i in range(n_ev):
         ev[i][0].record(cur)
-        layer_call(i % len(layers), write=False)
+        layer_call(i % len(layers), write=fused)
         ev[i][1].record(cur)
     torch.cuda.synchronize()
     launch_us_events = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
@@ -190,10 +198,13 @@ def main():
     qo_bytes = 2 * S * Hq * D * e
     decode_alg = kv_unique_tokens + qo_bytes + table_bytes + S * 4
     write_alg = 2 * 2 * S * Hkv * D * e + S * 4          # read new rows + write slots (K and V)
+    call_alg = decode_alg + (write_alg if not args.unfused else 0)
     step_kv = kv_logical * nlayers_step
     step_s = ms_per_step / 1e3
     value = step_kv / step_s / 1e9
-    achieved = decode_alg / (launch_us * 1e-6) / 1e9
+    achieved = call_alg / (launch_us * 1e-6) / 1e9
+    kernel_name = ("paged_decode_partition_kernel (fused cache write)" if not args.unfused
+                   else "paged_decode_partition_kernel")
 
     result = {
         "metric": "paged-decode KV read GB/s (% of MI355X HBM peak); decode tokens/s",
@@ -223,13 +234,13 @@ def main():
         "kv_bytes_per_step": step_kv,
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_partition_kernel",
+            "kernel": kernel_name,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "alg_bytes_per_launch": decode_alg,
+            "traffic": measured_traffic(args.workload, fused),
+            "alg_bytes_per_launch": call_alg,
             "launch_us": round(launch_us, 3),
             "launch_us_method": "hipgraph of back-to-back decode calls, events around the replays",
             "launch_us_events_eager": round(launch_us_events, 3),
@@ -240,6 +251,56 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, layers[:nlayers_step], args.cpu_seconds,
                                               kv_logical)
     print(json.dumps(result), flush=True)
+
+
+def kernel_source_digest():
+    """sha256 over the library's kernel sources: traffic counters recorded for
+    other sources are stale."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    here = os.path.dirname(os.path.abspath(__file__))
+    for path in sorted(glob.glob(os.path.join(here, "paged_kv_cache_206_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, fused):
+    """HBM bytes per decode call from the committed counter summary
+    (profiles/paged_decode_<workload>_hbm_traffic.md: FETCH_SIZE and WRITE_SIZE,
+    each calibrated against a plain copy), or None when there is none for
+    this kernel source."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"paged_decode_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip("` ")] = v.strip().strip("`")
+    key = "traffic_bytes_per_call_fused" if fused else "traffic_bytes_per_call_unfused"
+    if fields.get("kernel_source_sha256") != kernel_source_digest() or key not in fields:
+        return None
+    return int(float(fields[key]))
+
+
+def copy_probe(torch, dev, mib, steps):
+    """A plain copy of known size: each dispatch reads and writes mib MiB."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "dispatches": steps, "seconds_per_copy": dt,
+                      "gbs_read_plus_write": 2 * n / dt / 1e9}), flush=True)
 
 
 def unique_token_rows(wl):
@@ -278,8 +339,9 @@ def cpu_baseline(wl, layers, budget_s, kv_logical_per_layer):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{done} of {len(layers)} layers of the same step (cache write + decode, all "
-                  f"{wl.num_seqs} seqs), numpy fp64, BLAS limited to 1 thread, host copy untimed",
+        "sample": f"{done} layer passes (cache write + decode of all {wl.num_seqs} seqs; the step's "
+                  f"{len(layers)} layers in turn) until {budget_s:.0f} s were spent, numpy fp64, "
+                  f"BLAS limited to 1 thread, host copies untimed",
         "seconds": round(spent, 3),
         "tokens_per_s": round(wl.num_seqs * done / len(layers) / spent, 3),
         "host_cpus": os.cpu_count(),
@@ -287,10 +349,17 @@ def cpu_baseline(wl, layers, budget_s, kv_logical_per_layer):
 
 
 def _time_oracle(oracle, wl, layers, bits, bt, cl, slots, budget_s):
+    """Whole layers (cache write + decode of every sequence), cycling through
+    the step's layers until the budget is spent."""
     spent, done = 0.0, 0
-    for layer in layers:
-        host = [bits(t) for t in (layer.q, layer.k_cache, layer.v_cache)]
-        kv_new = (bits(layer.key), bits(layer.value)) if layer.key is not None else None
+    hosts = {}
+    while spent < budget_s:
+        li = done % len(layers)
+        layer = layers[li]
+        if li not in hosts:   # host copies, untimed
+            hosts[li] = ([bits(t) for t in (layer.q, layer.k_cache, layer.v_cache)],
+                         (bits(layer.key), bits(layer.value)) if layer.key is not None else None)
+        host, kv_new = hosts[li]
         t0 = time.perf_counter()
         kc, vc = host[1], host[2]
         if kv_new is not None:
@@ -298,8 +367,6 @@ def _time_oracle(oracle, wl, layers, bits, bt, cl, slots, budget_s):
         oracle.paged_decode(host[0], kc, vc, bt, cl, wl.scale, wl.dtype)
         spent += time.perf_counter() - t0
         done += 1
-        if spent >= budget_s:
-            break
     return spent, done
 
 
