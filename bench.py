@@ -95,7 +95,7 @@ def main():
     S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     maxlen = wl.max_context_len
     ws_bytes, part = mvk.workspace_size(S, Hq, Hkv, D, maxlen, args.partition)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)  # zero-filled before first use
     outs = [torch.empty_like(l.q) for l in layers]
     torch.cuda.synchronize()
 

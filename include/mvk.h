@@ -105,7 +105,11 @@ int32_t mvk_reshape_and_cache(const void* key, const void* value,
  * multiple of 16; 0 lets the library choose from num_seqs, num_kv_heads and
  * max_context_len). When a sequence spans more than one partition, each
  * partition's partial softmax state (running max, denominator, normalised
- * output; float32) goes to the workspace and a second kernel merges them.
+ * output; float32) goes to the workspace, and the partitions are merged either
+ * by a second kernel of the same call or, for skewed batches, by the last
+ * partition of a (sequence, KV head) to finish, counted in a 64 KiB counter
+ * region at the start of the workspace that holds nothing else. Skewed
+ * batches also keep a compact list of their non-empty partitions there.
  *
  *   *workspace_bytes          receives the size (0 when no split is needed).
  *   *chosen_partition_tokens  receives the partition length that the decode
@@ -161,8 +165,11 @@ int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads
  *   workspace     device scratch of workspace_bytes (from
  *                 mvk_paged_attention_workspace_size with the same sizes and
  *                 partition_tokens); may be NULL when that size is 0. Owned by
- *                 the caller; contents need no initialisation; must not be
- *                 shared by calls that may run concurrently.
+ *                 the caller. It must be zero-filled before its first use
+ *                 (e.g. hipMemset at allocation); every call that completes
+ *                 leaves it ready for the next one, so it can be reused
+ *                 without clearing. It must not be shared by calls that may
+ *                 run concurrently.
  *   head_dim 64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
  *   block_size 16.  num_seqs == 0 is a no-op.
  * Unused pool slots and the unread tail of a sequence's last block may hold

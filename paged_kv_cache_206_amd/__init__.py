@@ -172,8 +172,10 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     sequence s attends over it.
 
     `max_context_len` must bound context_lens; when omitted it is read from the
-    device (a synchronising copy). `workspace` (uint8, on the device) is
-    allocated through torch when needed and not given."""
+    device (a synchronising copy). `workspace` (uint8, on the device, at least
+    workspace_size() bytes) must be zero-filled before its first use; calls
+    leave it ready for the next call. It is allocated through torch when
+    needed and not given."""
     _require(q, "q", ndim=3)
     _require(k_cache, "k_cache", dtype=q.dtype, ndim=4)
     _require(v_cache, "v_cache", dtype=q.dtype, ndim=4)
@@ -208,8 +210,8 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     need, _ = workspace_size(S, hq, hkv, d, max_context_len, partition_tokens)
     ws_ptr, ws_bytes = None, 0
     if need:
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is None:   # zero-filled, as a workspace must be before its first use
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         _require(workspace, "workspace", dtype=torch.uint8)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     st = lib().mvk_paged_attention_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),

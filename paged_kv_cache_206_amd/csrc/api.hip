@@ -24,6 +24,12 @@ constexpr int32_t kMaxGridYZ = 65535;
 constexpr int64_t kGridLimit = 16384;
 // Workgroups (over all KV heads) that walk the work list.
 constexpr int64_t kListWorkgroups = 4096;
+// Any workspace starts with this many bytes of partition counters, one int32
+// per (sequence, KV head), and nothing else is ever stored there: every call
+// returns the counters it used to zero, so a workspace zero-filled once stays
+// valid for calls of any shape. Batches with more (sequence, KV head) pairs
+// than the region holds merge their partitions with a separate kernel.
+constexpr size_t kCounterRegion = 65536;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -59,10 +65,13 @@ struct Plan {
   int32_t partition_tokens;
   int32_t num_parts;
   int32_t waves;
+  int32_t head_fastest;
   bool work_list;
   int32_t list_workgroups;
-  size_t partial_bytes;    // partial (m, l, o) states, at the start of the workspace
-  size_t workspace_bytes;  // partial states + work list
+  size_t counter_bytes;    // the counter region at the start of the workspace
+  bool use_counters;       // merge partitions in the partition kernel
+  size_t partial_bytes;    // partial (m, l, o) states, after the counters
+  size_t workspace_bytes;  // counters + partial states + work list
 };
 
 int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -78,11 +87,14 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   int32_t p = partition_tokens ? partition_tokens
                                : default_partition(num_seqs, num_kv_heads, max_context_len);
   int32_t waves = default_waves(p);
+  int32_t head_fastest = 0;
+  int merge_mode = -1;  // -1: chosen below
 #ifdef MVK_TUNING
+  if (getenv("MVK_TUNE_MERGE")) merge_mode = atoi(getenv("MVK_TUNE_MERGE")) != 0;
+  if (getenv("MVK_TUNE_ORDER")) head_fastest = atoi(getenv("MVK_TUNE_ORDER"));
   if (!partition_tokens && getenv("MVK_TUNE_P")) p = atoi(getenv("MVK_TUNE_P"));
   if (getenv("MVK_TUNE_W")) waves = atoi(getenv("MVK_TUNE_W"));
-  if (p < kBlock || p > kMaxPartition || p % kBlock ||
-      (waves != 4 && waves != 8 && !(waves == 16 && num_q_heads / num_kv_heads <= 2)))
+  if (p < kBlock || p > kMaxPartition || p % kBlock || (waves != 4 && waves != 8))
     return MVK_ERR_INVALID_ARGUMENT;
 #endif
   int64_t parts = ((int64_t)max_context_len + p - 1) / p;
@@ -91,6 +103,7 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   plan->partition_tokens = p;
   plan->num_parts = (int32_t)parts;
   plan->waves = waves;
+  plan->head_fastest = head_fastest;
   plan->partial_bytes =
       parts > 1 ? (size_t)num_seqs * num_q_heads * (size_t)parts * (size_t)(head_dim + 2) * 4u : 0;
   const int64_t dense = (int64_t)num_seqs * parts * num_kv_heads;
@@ -98,8 +111,17 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   if (!plan->work_list && dense > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
   const int64_t per_head = (kListWorkgroups + num_kv_heads - 1) / num_kv_heads;
   plan->list_workgroups = (int32_t)(per_head < num_seqs * parts ? per_head : num_seqs * parts);
-  plan->workspace_bytes =
-      plan->partial_bytes + (plan->work_list ? (size_t)(1 + 2 * num_seqs * parts) * 4u : 0);
+  // Where partitions merge. In the partition kernel (the last partition of a
+  // (sequence, KV head) to finish merges) saves the merge kernel's launch but
+  // makes every partition wait for its partial state to reach memory; that
+  // pays off when few sequences are split, i.e. in work-list mode, and costs
+  // more than it saves when every sequence is split (dense grids).
+  const bool merge_in_kernel = merge_mode < 0 ? plan->work_list : merge_mode != 0;
+  plan->counter_bytes = parts > 1 ? kCounterRegion : 0;
+  plan->use_counters = parts > 1 && merge_in_kernel &&
+                       (size_t)num_seqs * num_kv_heads * 4u <= kCounterRegion;
+  plan->workspace_bytes = plan->counter_bytes + plan->partial_bytes +
+                          (plan->work_list ? (size_t)(1 + 2 * num_seqs * parts) * 4u : 0);
   return MVK_OK;
 }
 
@@ -206,9 +228,11 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
   a.new_value = new_value;
   a.slot_mapping = slot_mapping;
   const size_t n_state = (size_t)num_seqs * num_q_heads * (size_t)plan.num_parts;
-  a.ws_ml = plan.partial_bytes ? (float*)workspace : nullptr;
-  a.ws_o = plan.partial_bytes ? (float*)workspace + n_state * 2 : nullptr;
-  a.items = plan.work_list ? (int32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
+  char* partials = (char*)workspace + plan.counter_bytes;
+  a.ws_ml = plan.partial_bytes ? (float*)partials : nullptr;
+  a.ws_o = plan.partial_bytes ? (float*)partials + n_state * 2 : nullptr;
+  a.counters = plan.use_counters ? (int32_t*)workspace : nullptr;
+  a.items = plan.work_list ? (int32_t*)(partials + plan.partial_bytes) : nullptr;
   a.list_workgroups = plan.list_workgroups;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -220,6 +244,7 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
   a.partition_tokens = plan.partition_tokens;
   a.num_parts = plan.num_parts;
   a.waves = plan.waves;
+  a.head_fastest = plan.head_fastest;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;
   hipError_t err = mvk::launch_paged_decode(a, (hipStream_t)stream);

@@ -68,6 +68,17 @@ __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
+// Device-coherent float store / load (relaxed atomics at device scope): they
+// bypass the per-XCD L2's non-coherent state, so a value published by one
+// workgroup is seen by a workgroup on another XCD without any cache-wide
+// writeback or invalidate.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float collect(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Cross-lane moves inside a 16-lane DPP row.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {

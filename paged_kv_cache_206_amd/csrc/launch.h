@@ -28,7 +28,10 @@ struct DecodeArgs {
   int32_t num_blocks, max_blocks_per_seq, max_context_len;
   int32_t partition_tokens, num_parts;
   int32_t waves;     // waves per workgroup (4 or 8)
+  int32_t head_fastest;  // grid order (see Shape)
   int32_t* items;    // work list (count, then (seq, part) pairs); nullptr = grid mode
+  int32_t* counters; // per (seq, KV head) partition counters (zero between calls), or
+                     // nullptr: partitions are merged by a separate kernel
   int32_t list_workgroups;  // workgroups per KV head in work-list mode
   float scale_log2;  // scale * log2(e): logits are kept in base-2 units
   int32_t dtype;

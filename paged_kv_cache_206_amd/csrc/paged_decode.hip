@@ -10,9 +10,15 @@
 // serves all g = Hq/Hkv query heads of the GQA group, so each K/V row fetched
 // from HBM is used g times. The partition's blocks are dealt round-robin to
 // the W waves of the workgroup; every wave first fetches all of its block-table
-// entries with one vector load (issued together with the context-length load),
-// then streams its blocks with the next block's K/V loads in flight while the
+// entries with one vector load (issued together with the context length, the
+// query rows and the new K/V row, so the prologue costs one round trip), then
+// streams its blocks with the next blocks' K/V loads in flight while the
 // current block is computed.
+//
+// Fused cache write (both policies): when the call brings the step's new K/V
+// rows, the block holding a sequence's new slot takes that row from registers
+// instead of memory, and wave 0 of partition 0 stores it once (the store of
+// record), so attention never waits for its own write.
 //
 // Per-block compute, two policies:
 //  * MFMA (g >= 4): logits as S^T = K Q^T with v_mfma_f32_16x16x32 (16 tokens x
@@ -43,6 +49,10 @@ namespace mvk {
 constexpr uint32_t kXcds = 8;          // accelerator complex dies of an MI355X
 constexpr float kNegBig = -1.0e30f;   // "no token seen yet" (finite: 2^(a-b) never sees inf-inf)
 constexpr float kLazyRescale = 8.0f;  // p = 2^(z - m) may grow up to 2^8 before rescaling
+// Blocks whose loads are in flight per wave. Two keep HBM busy with two
+// waves per SIMD; four (measured) only add registers and delay the first
+// block's compute.
+constexpr int kPrefetch = 2;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -80,15 +90,14 @@ constexpr uint32_t kPermHiHalves = 0x07060302u;
 struct Shape {
   int32_t num_kv_heads, num_blocks, max_blocks, max_context_len, partition_tokens, num_parts;
   float scale_log2;
+  int32_t head_fastest;  // grid order: 1 = (KV head, sequence, partition), 0 = (sequence, KV head, partition)
 };
 
-// Optional fused cache write: row s of key/value ([S, Hkv, D]) is sequence
-// s's token of this step, stored at flat slot slots[s] (negative = none).
-struct NewRows {
-  const uint16_t* key;
-  const uint16_t* value;
-  const int32_t* slots;
-};
+// Optional fused cache write: row s of new_key/new_value ([S, Hkv, D]) is
+// sequence s's token of this step, stored at flat slot slots[s] (negative =
+// none). Passed as separate __restrict__ kernel arguments: restrict on struct
+// members is not seen, and a possibly-aliased slot would be re-read through
+// the vector path with a wait on every load before it.
 
 // ------------------------------------------------------------ MFMA policy
 template <int DT, int D, int G>
@@ -109,6 +118,27 @@ struct MfmaPolicy {
   float m, lsum;
   int r16, q4;
   uint32_t koff, voff;  // per-lane byte offsets inside a block (loop invariant)
+  uint4 nk[NKS];        // new K row: the chunks a lane of token row r16 holds
+  VT nv;                // new V row: the chunk a lane of quarter q4 holds
+  int row_new;          // offset of the new row inside its block
+
+  // Fetch this lane's chunks of the step's new K/V row of this KV head; the
+  // block that holds it takes these values for that row instead of memory's.
+  __device__ __forceinline__ void load_new_row(const uint16_t* key_row, const uint16_t* value_row) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) nk[ks] = *(const uint4*)(key_row + 32 * ks + 8 * q4);
+    nv = *(const VT*)(value_row + VW * r16);
+  }
+
+  // Store the new row: the 4 lanes of token row 0 hold all of K, the 16
+  // lanes of quarter 0 all of V.
+  __device__ __forceinline__ void store_new_row(uint16_t* k_dst, uint16_t* v_dst) const {
+    if (r16 == 0) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) *(uint4*)(k_dst + 32 * ks + 8 * q4) = nk[ks];
+    }
+    if (q4 == 0) *(VT*)(v_dst + VW * r16) = nv;
+  }
 
   __device__ __forceinline__ void init(const uint16_t* q, size_t q_row0, int lane,
                                        uint32_t row_bytes) {
@@ -141,10 +171,17 @@ struct MfmaPolicy {
     }
   }
 
-  // `sub` (substitute a new row) is never set for this policy: fused calls
-  // with g >= 4 store the new rows with the cache-write kernel first.
   __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub) {
-    (void)sub;
+    if (sub) {  // this block holds the step's new row
+      if (r16 == row_new) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) f.k[ks] = nk[ks];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * q4 + i == row_new) f.v[i] = nv;
+      }
+    }
     using M = Mma<DT>;
     using E = Elem<DT>;
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -237,13 +274,19 @@ struct ValuPolicy {
   uint4 nk, nv;  // this lane's chunk of the step's new K/V row (fused cache write)
   int row_new;   // offset of the new row inside its block
 
-  // Load chunk c of the new K/V row of this KV head; the block that holds it
-  // will take these values for that row instead of what memory holds.
-  __device__ __forceinline__ void set_new_row(const uint16_t* key_row, const uint16_t* value_row,
-                                              int row) {
+  // Fetch chunk c of the step's new K/V row of this KV head; the block that
+  // holds it takes these values for that row instead of memory's.
+  __device__ __forceinline__ void load_new_row(const uint16_t* key_row, const uint16_t* value_row) {
     nk = *(const uint4*)(key_row + c * 8);
     nv = *(const uint4*)(value_row + c * 8);
-    row_new = row;
+  }
+
+  // Store the new row of this KV head (lanes of row group 0 cover it).
+  __device__ __forceinline__ void store_new_row(uint16_t* k_dst, uint16_t* v_dst) const {
+    if (rg == 0) {
+      *(uint4*)(k_dst + c * 8) = nk;
+      *(uint4*)(v_dst + c * 8) = nv;
+    }
   }
 
   __device__ __forceinline__ void init(const uint16_t* q, size_t q_row0, int lane,
@@ -360,14 +403,15 @@ struct ValuPolicy {
 // [part*P, min((part+1)*P, L))): the final row if the context fits in one
 // partition, else this partition's partial state. Every wave of the workgroup
 // calls it with the same arguments (it contains a barrier).
-template <int DT, int D, int G, int W, bool USE_MFMA, bool FUSED>
+template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED>
 __device__ __forceinline__ void decode_item(
     int s, int h, int part, uint16_t* __restrict__ out, float* __restrict__ ws_ml,
     float* __restrict__ ws_o, const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
     uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, const Shape& sh, const NewRows& nr,
-    float (*sm_o)[G * D], float (*sm_m)[G], float (*sm_l)[G]) {
-  static_assert(!(FUSED && USE_MFMA), "fused cache write runs with the VALU policy only");
+    const int32_t* __restrict__ context_lens, const Shape& sh,
+    const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
+    const int32_t* __restrict__ slots, int32_t* __restrict__ counters, float (*sm_o)[G * D],
+    float (*sm_m)[G], float (*sm_l)[G], int* sm_last) {
   using Policy = typename std::conditional<USE_MFMA, MfmaPolicy<DT, D, G>, ValuPolicy<DT, D, G>>::type;
   using E = Elem<DT>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -376,37 +420,36 @@ __device__ __forceinline__ void decode_item(
   const int t_begin = part * P;
   const int b_begin = t_begin / kBlockTokens;
 
-  // This wave's table entries (lane k <- block b_begin + wave + k*W), fetched
-  // together with the context length; the row is read only below max_blocks,
-  // and entries past the context are never used.
+  // Prologue: every load it needs (context length, fused slot, this wave's
+  // table entries, the query rows, the step's new K/V row) is issued before
+  // anything waits on one of them, so together they cost one memory round
+  // trip. Lane k takes table entry b_begin + wave + k*W; the row is read only
+  // below max_blocks, and entries past the context are never used.
+  const int len = context_lens[s];
+  int slot = -1;
+  if constexpr (FUSED) slot = slots[s];
   const int part_blocks = min(P / kBlockTokens, sh.max_blocks - b_begin);
   const int32_t* table = block_tables + (size_t)s * sh.max_blocks;
   int ent = 0;
   if (wave + lane * W < part_blocks) ent = table[b_begin + wave + lane * W];
-
-  const int L = min(context_lens[s], sh.max_context_len);
   const int Hq = sh.num_kv_heads * G;
   const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;  // one token row of the pool
-  int blk_new = -1, row_new = 0;
-  const uint16_t* new_k = nullptr;
-  const uint16_t* new_v = nullptr;
-  if constexpr (FUSED) {
-    const int slot = nr.slots[s];
-    if (slot >= 0 && slot < sh.num_blocks * kBlockTokens) {
-      blk_new = slot / kBlockTokens;
-      row_new = slot % kBlockTokens;
-      const size_t src = ((size_t)s * sh.num_kv_heads + h) * D;
-      new_k = nr.key + src;
-      new_v = nr.value + src;
-      // the store of record of this KV head's slice: one wave of partition 0
-      if (part == 0 && wave == 0 && lane < D / 8) {
-        const size_t dst = (size_t)slot * sh.num_kv_heads * D + (size_t)h * D + lane * 8;
-        *(uint4*)(k_cache + dst) = *(const uint4*)(new_k + lane * 8);
-        *(uint4*)(v_cache + dst) = *(const uint4*)(new_v + lane * 8);
-      }
-    }
-  }
+  const size_t new_src = ((size_t)s * sh.num_kv_heads + h) * D;
+  Policy pol;
+  pol.init(q, (size_t)s * Hq + (size_t)h * G, lane, row_bytes);
+  if constexpr (FUSED) pol.load_new_row(new_key + new_src, new_value + new_src);
+
+  const int L = min(len, sh.max_context_len);
+  const bool has_new = FUSED && slot >= 0 && slot < sh.num_blocks * kBlockTokens;
+  const int blk_new = has_new ? slot / kBlockTokens : -1;
+  if constexpr (FUSED) pol.row_new = has_new ? slot % kBlockTokens : -1;
+  const size_t new_dst = (size_t)(has_new ? slot : 0) * sh.num_kv_heads * D + (size_t)h * D;
+  // the store of record of this KV head's slice: wave 0 of partition 0
+  const bool writer = has_new && part == 0 && wave == 0;
   if (t_begin >= L) {  // uniform over the workgroup
+    if constexpr (FUSED) {
+      if (writer) pol.store_new_row(k_cache + new_dst, v_cache + new_dst);
+    }
     if (part == 0) {   // empty context: the row is defined as zeros
       const size_t row0 = ((size_t)s * Hq + (size_t)h * G) * D;
       for (int idx = threadIdx.x; idx < G * D; idx += W * 64) out[row0 + idx] = 0;
@@ -416,49 +459,50 @@ __device__ __forceinline__ void decode_item(
   const int t_end = min(t_begin + P, L);
   const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
   const int my_blocks = nblk > wave ? (nblk - wave + W - 1) / W : 0;
-
   const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
-  Policy pol;
-  pol.init(q, (size_t)s * Hq + (size_t)h * G, lane, row_bytes);
-  if constexpr (FUSED) {
-    if (blk_new >= 0) pol.set_new_row(new_k, new_v, row_new);
-  }
 
   const char* kbase = (const char*)(k_cache + (size_t)h * D);
   const char* vbase = (const char*)(v_cache + (size_t)h * D);
   if (my_blocks > 0) {
-    // Two fragments in ping-pong: the next block's loads go out before the
-    // current block is computed, and no register copy of in-flight data is
-    // ever needed. Each block is read through a buffer descriptor covering
+    // NPF fragments in rotation: the loads of the next NPF-1 blocks are in
+    // flight while a block is computed, and no register copy of in-flight
+    // data is ever needed (the rotation is unrolled, so every fragment index
+    // is static). Each block is read through a buffer descriptor covering
     // only its rows that hold context tokens, so rows past the context (any
-    // bits, NaN included) read as zeros. The step after the last block issues
-    // its loads through an empty descriptor: they return zeros without
-    // touching memory, which keeps the load count of every step the same.
-    typename Policy::Frag fa, fb;
+    // bits, NaN included) read as zeros. Steps past the last block issue their
+    // loads through an empty descriptor: they return zeros without touching
+    // memory, which keeps the load count of every step the same.
+    typename Policy::Frag f[NPF];
     auto tok_of = [&](int k) { return (b_begin + wave + k * W) * kBlockTokens; };
     auto block_of = [&](int k) {
       int blk = __builtin_amdgcn_readlane(ent, min(k, my_blocks - 1));
       return ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
     };
-    auto load_block = [&](typename Policy::Frag& f, int k) {
+    auto load_block = [&](typename Policy::Frag& fr, int k) {
       const bool real = k < my_blocks;
       const int blk = block_of(k);
       k = min(k, my_blocks - 1);
       const int rows = min(kBlockTokens, t_end - tok_of(k));
       const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
       const size_t o = (size_t)blk * block_bytes;
-      pol.load(f, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
+      pol.load(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
     };
     auto is_new = [&](int k) { return FUSED && block_of(k) == blk_new; };
-    load_block(fa, 0);
-    for (int k = 0;;) {
-      load_block(fb, k + 1);
-      pol.process(fa, tok_of(k), t_end, sh.scale_log2, is_new(k));
-      if (++k >= my_blocks) break;
-      load_block(fa, k + 1);
-      pol.process(fb, tok_of(k), t_end, sh.scale_log2, is_new(k));
-      if (++k >= my_blocks) break;
+#pragma unroll
+    for (int j = 0; j < NPF - 1; ++j) load_block(f[j], j);
+    for (int k0 = 0;; k0 += NPF) {
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        const int k = k0 + j;
+        load_block(f[(j + NPF - 1) % NPF], k + NPF - 1);
+        pol.process(f[j], tok_of(k), t_end, sh.scale_log2, is_new(k));
+        if (k + 1 >= my_blocks) goto blocks_done;
+      }
     }
+  blocks_done:;
+  }
+  if constexpr (FUSED) {
+    if (writer) pol.store_new_row(k_cache + new_dst, v_cache + new_dst);
   }
   pol.to_lds(sm_m[wave], sm_l[wave], sm_o[wave]);
   __syncthreads();
@@ -484,11 +528,53 @@ __device__ __forceinline__ void decode_item(
       out[hq * D + d] = E::round(r);
     } else {
       const size_t slot = hq * sh.num_parts + part;
-      ws_o[slot * D + d] = r;
+      publish(ws_o + slot * D + d, r);
       if (d == 0) {
-        ws_ml[slot * 2] = mm;
-        ws_ml[slot * 2 + 1] = lsum;
+        publish(ws_ml + slot * 2, mm);
+        publish(ws_ml + slot * 2 + 1, lsum);
       }
+    }
+  }
+
+  // Several partitions, merged in this launch: each workgroup publishes its
+  // partial state and counts itself in; the last of the sequence's partitions
+  // to arrive (whichever it is) merges all of them in partition order, so the
+  // result does not depend on arrival order, and resets the counter to zero
+  // for the next call. No workgroup ever waits for another.
+  //
+  // The partial states are written and read only with device-coherent
+  // accesses (publish / collect), so no cache-wide fence is needed: a device
+  // release or acquire fence would write back or invalidate this XCD's whole
+  // L2, which costs more than the merge saves. Waiting for every store of the
+  // workgroup to complete before the counter update orders them before it.
+  if (parts_of_seq > 1 && counters != nullptr) {
+    int32_t* ctr = counters + (size_t)s * sh.num_kv_heads + h;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int done = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *sm_last = done == parts_of_seq - 1;
+    }
+    __syncthreads();
+    if (*sm_last) {
+      for (int idx = threadIdx.x; idx < G * D; idx += W * 64) {
+        const int j = idx / D;
+        const int d = idx % D;
+        const size_t hq = (size_t)s * Hq + (size_t)h * G + j;
+        const float* ml = ws_ml + hq * sh.num_parts * 2;
+        const float* o = ws_o + hq * sh.num_parts * D + d;
+        float mm = -INFINITY;
+        for (int p = 0; p < parts_of_seq; ++p) mm = fmaxf(mm, collect(ml + 2 * p));
+        float acc = 0.0f, tot = 0.0f;
+#pragma unroll 4
+        for (int p = 0; p < parts_of_seq; ++p) {
+          const float w = collect(ml + 2 * p + 1) * fast_exp2(collect(ml + 2 * p) - mm);
+          acc = fmaf(w, collect(o + (size_t)p * D), acc);
+          tot += w;
+        }
+        out[hq * D + d] = E::round(tot > 0.0f ? acc / tot : 0.0f);
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -499,16 +585,18 @@ __device__ __forceinline__ void decode_item(
 // Work-list mode: grid (X, Hkv); the plan kernel has written the count and
 // the (sequence, partition) items of all non-empty partitions, and workgroup
 // x takes items x, x+X, ... so no workgroup is launched for nothing.
-template <int DT, int D, int G, int W, bool USE_MFMA, bool FUSED>
-__global__ __launch_bounds__(W * 64) void paged_decode_partition_kernel(
+template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void paged_decode_partition_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
     uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ items, Shape sh,
-    NewRows nr) {
+    const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
+    const int32_t* __restrict__ slots, int32_t* __restrict__ counters) {
   __shared__ float sm_o[W][G * D];
   __shared__ float sm_m[W][G];
   __shared__ float sm_l[W][G];
+  __shared__ int sm_last;
   if (items == nullptr) {
     // Workgroups are dealt round-robin to the 8 XCDs in dispatch order; remap
     // so that each XCD runs a contiguous range of (sequence fastest, then KV
@@ -518,21 +606,24 @@ __global__ __launch_bounds__(W * 64) void paged_decode_partition_kernel(
     const uint32_t i = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const uint32_t xcd = i % kXcds, per = n / kXcds, rem = n % kXcds;
     const uint32_t v = xcd * per + min(xcd, rem) + i / kXcds;
-    const int s = v % gridDim.x;
-    const int h = (v / gridDim.x) % gridDim.y;
-    const int part = v / (gridDim.x * gridDim.y);
-    decode_item<DT, D, G, W, USE_MFMA, FUSED>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
-                                               block_tables, context_lens, sh, nr, sm_o, sm_m,
-                                               sm_l);
+    const int S = gridDim.x, H = gridDim.y;
+    const int s = sh.head_fastest ? (v / H) % S : v % S;
+    const int h = sh.head_fastest ? v % H : (v / S) % H;
+    const int part = v / (S * H);
+    decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
+                                               block_tables, context_lens, sh, new_key,
+                                               new_value, slots, counters, sm_o, sm_m, sm_l,
+                                               &sm_last);
     return;
   }
   const int count = items[0];
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int s = items[1 + 2 * i];
     const int part = items[2 + 2 * i];
-    decode_item<DT, D, G, W, USE_MFMA, FUSED>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache,
-                                               v_cache, block_tables, context_lens, sh, nr, sm_o,
-                                               sm_m, sm_l);
+    decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache,
+                                               v_cache, block_tables, context_lens, sh, new_key,
+                                               new_value, slots, counters, sm_o, sm_m, sm_l,
+                                               &sm_last);
     __syncthreads();  // the LDS of this item is read before the next item writes it
   }
 }
@@ -657,11 +748,10 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_kernel(
   }
 }
 
-template <int DT, int D, int G, int W, bool USE_MFMA, bool FUSED>
+template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   Shape sh{a.num_kv_heads, a.num_blocks, a.max_blocks_per_seq, a.max_context_len,
-           a.partition_tokens, a.num_parts, a.scale_log2};
-  NewRows nr{(const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.slot_mapping};
+           a.partition_tokens, a.num_parts, a.scale_log2, a.head_fastest};
   dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_parts);
   if (a.items != nullptr) {
     hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.items,
@@ -670,12 +760,14 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     grid = dim3((unsigned)a.list_workgroups, (unsigned)a.num_kv_heads, 1u);
   }
-  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, W, USE_MFMA, FUSED>), grid,
+  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, W, NPF, USE_MFMA, FUSED>), grid,
                      dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
                      (const uint16_t*)a.q, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache,
-                     a.block_tables, a.context_lens, (const int32_t*)a.items, sh, nr);
+                     a.block_tables, a.context_lens, (const int32_t*)a.items, sh,
+                     (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.slot_mapping,
+                     a.counters);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.num_parts <= 1) return err;
+  if (err != hipSuccess || a.num_parts <= 1 || a.counters != nullptr) return err;
   dim3 mgrid((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
   hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, G>), mgrid, dim3(kMergeThreads), 0, stream,
                      (uint16_t*)a.out, a.ws_ml, a.ws_o, a.context_lens, a.num_kv_heads,
@@ -686,34 +778,13 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 template <int DT, int D, int G>
 static hipError_t launch_waves(const DecodeArgs& a, hipStream_t stream) {
   constexpr bool kMfma = G >= 4;  // g <= 2: VALU keeps up with HBM; g >= 4: MFMA
-  if constexpr (kMfma) {
-    if (a.new_key != nullptr) {
-      // fused call with the MFMA policy: the cache-write kernel goes first on
-      // the same stream, then attention reads the stored rows
-      const int64_t row_vecs = (int64_t)a.num_kv_heads * D * 2 / 16;
-      hipError_t err = launch_cache_write(a.new_key, a.new_value, (void*)a.k_cache,
-                                          (void*)a.v_cache, a.slot_mapping, a.num_seqs,
-                                          (int32_t)row_vecs, (int64_t)a.num_blocks * kBlockTokens,
-                                          stream);
-      if (err != hipSuccess) return err;
-    }
-    switch (a.waves) {
-      case 4: return launch_typed<DT, D, G, 4, true, false>(a, stream);
-      case 8: return launch_typed<DT, D, G, 8, true, false>(a, stream);
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    const bool fused = a.new_key != nullptr;
-    switch (a.waves) {
-      case 4: return fused ? launch_typed<DT, D, G, 4, false, true>(a, stream)
-                           : launch_typed<DT, D, G, 4, false, false>(a, stream);
-      case 8: return fused ? launch_typed<DT, D, G, 8, false, true>(a, stream)
-                           : launch_typed<DT, D, G, 8, false, false>(a, stream);
-      // 16 waves fit one CU only at <= 128 VGPRs: VALU policy only
-      case 16: return fused ? launch_typed<DT, D, G, 16, false, true>(a, stream)
-                            : launch_typed<DT, D, G, 16, false, false>(a, stream);
-      default: return hipErrorInvalidValue;
-    }
+  const bool fused = a.new_key != nullptr;
+  switch (a.waves) {
+    case 4: return fused ? launch_typed<DT, D, G, 4, kPrefetch, kMfma, true>(a, stream)
+                         : launch_typed<DT, D, G, 4, kPrefetch, kMfma, false>(a, stream);
+    case 8: return fused ? launch_typed<DT, D, G, 8, kPrefetch, kMfma, true>(a, stream)
+                         : launch_typed<DT, D, G, 8, kPrefetch, kMfma, false>(a, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

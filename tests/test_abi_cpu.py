@@ -130,12 +130,12 @@ def test_workspace_size(mvk):
     nbytes, p = mvk.workspace_size(4, 4, 2, 64, 45)
     assert nbytes == 0 and p >= 48 and p % 16 == 0
     nbytes, p = mvk.workspace_size(32, 32, 8, 128, 32768, 512)
-    assert p == 512 and nbytes == 32 * 32 * 64 * (128 + 2) * 4
+    assert p == 512 and nbytes == 65536 + 32 * 32 * 64 * (128 + 2) * 4   # counters + partials
     nbytes, p = mvk.workspace_size(2, 2, 1, 64, 0)
     assert nbytes == 0
     # skewed batch: the dense grid would be huge, so a work list is appended
     nbytes, p = mvk.workspace_size(512, 16, 8, 128, 131072, 1024)
     parts = 131072 // 1024
-    assert nbytes == 512 * 16 * parts * 130 * 4 + (1 + 2 * 512 * parts) * 4
+    assert nbytes == 65536 + 512 * 16 * parts * 130 * 4 + (1 + 2 * 512 * parts) * 4
     with pytest.raises(mvk.MvkError):
         mvk.workspace_size(2, 3, 2, 64, 10)

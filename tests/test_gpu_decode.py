@@ -187,3 +187,31 @@ def test_work_list_mode(dtype, d, g, p):
     out, _ = parity(wl, partition_tokens=p)
     zero_rows = out[lens == 0]
     assert torch.all(zero_rows == 0)
+
+
+def test_workspace_reused_across_calls():
+    """One zero-filled workspace serves many calls of different shapes and
+    partition lengths, alternating dense grids (merge kernel) and work lists
+    (in-launch merge, rounds 1, 3 and 5: more than 16384 dense workgroups):
+    the per-(sequence, KV head) counters of the in-launch merge return to
+    zero after every call, whatever the shape of the next."""
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator().manual_seed(77)
+    for rnd in range(6):
+        n = [40, 300, 120, 400, 60, 250][rnd]
+        lens = torch.randint(1, 900, (n,), generator=gen).tolist()
+        g = [1, 2, 4, 8, 2, 4][rnd]
+        wl = custom("bf16", lens, 2 * g, 2, 128, seed=100 + rnd)
+        p = [16, 16, 32, 16, 48, 16][rnd]
+        nbytes, _ = mvk.workspace_size(n, 2 * g, 2, 128, wl.max_context_len, p)
+        assert nbytes <= ws.numel()
+        ref = oracle_decode(wl)
+        gw = wl.to("cuda")
+        l = gw.layers[0]
+        for _ in range(2):   # the same call twice on the same workspace
+            out = mvk.paged_attention_decode(l.q, l.k_cache, l.v_cache, gw.block_tables,
+                                             gw.context_lens, wl.scale,
+                                             max_context_len=wl.max_context_len,
+                                             partition_tokens=p, workspace=ws)
+            torch.cuda.synchronize()
+            assert max_err(out, ref, "bf16") <= TOL["bf16"], (rnd, p)

@@ -44,7 +44,7 @@ def test_graph_replay_matches_eager(case, fused):
     bt, cl, slots = wl.block_tables, wl.context_lens, wl.slot_mapping
     nbytes, _ = mvk.workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                    maxlen, p)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     eager = [torch.empty_like(l.q) for l in wl.layers]
     run_step(wl, bt, cl, slots, eager, p, ws, maxlen, fused)
     torch.cuda.synchronize()
