@@ -118,27 +118,7 @@ struct MfmaPolicy {
   float m, lsum;
   int r16, q4;
   uint32_t koff, voff;  // per-lane byte offsets inside a block (loop invariant)
-  uint4 nk[NKS];        // new K row: the chunks a lane of token row r16 holds
-  VT nv;                // new V row: the chunk a lane of quarter q4 holds
-  int row_new;          // offset of the new row inside its block
-
-  // Fetch this lane's chunks of the step's new K/V row of this KV head; the
-  // block that holds it takes these values for that row instead of memory's.
-  __device__ __forceinline__ void load_new_row(const uint16_t* key_row, const uint16_t* value_row) {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) nk[ks] = *(const uint4*)(key_row + 32 * ks + 8 * q4);
-    nv = *(const VT*)(value_row + VW * r16);
-  }
-
-  // Store the new row: the 4 lanes of token row 0 hold all of K, the 16
-  // lanes of quarter 0 all of V.
-  __device__ __forceinline__ void store_new_row(uint16_t* k_dst, uint16_t* v_dst) const {
-    if (r16 == 0) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) *(uint4*)(k_dst + 32 * ks + 8 * q4) = nk[ks];
-    }
-    if (q4 == 0) *(VT*)(v_dst + VW * r16) = nv;
-  }
+  int row_new;          // offset of the step's new row inside its block (fused write)
 
   __device__ __forceinline__ void init(const uint16_t* q, size_t q_row0, int lane,
                                        uint32_t row_bytes) {
@@ -171,15 +151,17 @@ struct MfmaPolicy {
     }
   }
 
-  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub) {
-    if (sub) {  // this block holds the step's new row
+  // nk/nv: the step's new K/V row of this KV head in LDS, as 16-byte chunks
+  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub,
+                                          const uint4* nk, const uint4* nv) {
+    if (sub) {  // this block holds the new row: take it from LDS, not memory
       if (r16 == row_new) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) f.k[ks] = nk[ks];
+        for (int ks = 0; ks < NKS; ++ks) f.k[ks] = nk[4 * ks + q4];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (4 * q4 + i == row_new) f.v[i] = nv;
+        if (4 * q4 + i == row_new) f.v[i] = ((const VT*)nv)[r16];
       }
     }
     using M = Mma<DT>;
@@ -271,23 +253,7 @@ struct ValuPolicy {
   float m[G], l[G], acc[G][8];
   int rg, c;
   uint32_t off;  // per-lane byte offset inside a block (loop invariant)
-  uint4 nk, nv;  // this lane's chunk of the step's new K/V row (fused cache write)
-  int row_new;   // offset of the new row inside its block
-
-  // Fetch chunk c of the step's new K/V row of this KV head; the block that
-  // holds it takes these values for that row instead of memory's.
-  __device__ __forceinline__ void load_new_row(const uint16_t* key_row, const uint16_t* value_row) {
-    nk = *(const uint4*)(key_row + c * 8);
-    nv = *(const uint4*)(value_row + c * 8);
-  }
-
-  // Store the new row of this KV head (lanes of row group 0 cover it).
-  __device__ __forceinline__ void store_new_row(uint16_t* k_dst, uint16_t* v_dst) const {
-    if (rg == 0) {
-      *(uint4*)(k_dst + c * 8) = nk;
-      *(uint4*)(v_dst + c * 8) = nv;
-    }
-  }
+  int row_new;   // offset of the step's new row inside its block (fused write)
 
   __device__ __forceinline__ void init(const uint16_t* q, size_t q_row0, int lane,
                                        uint32_t row_bytes) {
@@ -315,14 +281,16 @@ struct ValuPolicy {
     }
   }
 
-  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub) {
+  // nk/nv: the step's new K/V row of this KV head in LDS, as 16-byte chunks
+  __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub,
+                                          const uint4* nk, const uint4* nv) {
     using E = Elem<DT>;
-    if (sub) {  // this block holds the step's new row
+    if (sub) {  // this block holds the new row: take it from LDS, not memory
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
         if (i * RG + rg == row_new) {
-          f.k[i] = nk;
-          f.v[i] = nv;
+          f.k[i] = nk[c];
+          f.v[i] = nv[c];
         }
       }
     }
@@ -411,7 +379,7 @@ __device__ __forceinline__ void decode_item(
     const int32_t* __restrict__ context_lens, const Shape& sh,
     const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
     const int32_t* __restrict__ slots, int32_t* __restrict__ counters, float (*sm_o)[G * D],
-    float (*sm_m)[G], float (*sm_l)[G], int* sm_last) {
+    float (*sm_m)[G], float (*sm_l)[G], int* sm_last, uint4* sm_nk, uint4* sm_nv) {
   using Policy = typename std::conditional<USE_MFMA, MfmaPolicy<DT, D, G>, ValuPolicy<DT, D, G>>::type;
   using E = Elem<DT>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -437,7 +405,16 @@ __device__ __forceinline__ void decode_item(
   const size_t new_src = ((size_t)s * sh.num_kv_heads + h) * D;
   Policy pol;
   pol.init(q, (size_t)s * Hq + (size_t)h * G, lane, row_bytes);
-  if constexpr (FUSED) pol.load_new_row(new_key + new_src, new_value + new_src);
+  // The step's new K/V row of this KV head: wave 0 fetches it here and stages
+  // it in LDS below, where the block that holds it takes it from (so it does
+  // not occupy registers through the block loop).
+  uint4 nk16 = make_uint4(0u, 0u, 0u, 0u), nv16 = nk16;
+  if constexpr (FUSED) {
+    if (wave == 0 && lane < D / 8) {
+      nk16 = *(const uint4*)(new_key + new_src + lane * 8);
+      nv16 = *(const uint4*)(new_value + new_src + lane * 8);
+    }
+  }
 
   const int L = min(len, sh.max_context_len);
   const bool has_new = FUSED && slot >= 0 && slot < sh.num_blocks * kBlockTokens;
@@ -448,7 +425,10 @@ __device__ __forceinline__ void decode_item(
   const bool writer = has_new && part == 0 && wave == 0;
   if (t_begin >= L) {  // uniform over the workgroup
     if constexpr (FUSED) {
-      if (writer) pol.store_new_row(k_cache + new_dst, v_cache + new_dst);
+      if (writer && lane < D / 8) {
+        *(uint4*)(k_cache + new_dst + lane * 8) = nk16;
+        *(uint4*)(v_cache + new_dst + lane * 8) = nv16;
+      }
     }
     if (part == 0) {   // empty context: the row is defined as zeros
       const size_t row0 = ((size_t)s * Hq + (size_t)h * G) * D;
@@ -461,48 +441,61 @@ __device__ __forceinline__ void decode_item(
   const int my_blocks = nblk > wave ? (nblk - wave + W - 1) / W : 0;
   const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
 
+  if constexpr (FUSED) {
+    if (wave == 0 && lane < D / 8) {
+      sm_nk[lane] = nk16;
+      sm_nv[lane] = nv16;
+    }
+  }
+
   const char* kbase = (const char*)(k_cache + (size_t)h * D);
   const char* vbase = (const char*)(v_cache + (size_t)h * D);
+  // NPF fragments in rotation: the loads of the next NPF-1 blocks are in
+  // flight while a block is computed, and no register copy of in-flight data
+  // is ever needed (the rotation is unrolled, so every fragment index is
+  // static). Each block is read through a buffer descriptor covering only its
+  // rows that hold context tokens, so rows past the context (any bits, NaN
+  // included) read as zeros. Steps past the last block issue their loads
+  // through an empty descriptor: they return zeros without touching memory,
+  // which keeps the load count of every step the same.
+  typename Policy::Frag f[NPF];
+  auto tok_of = [&](int k) { return (b_begin + wave + k * W) * kBlockTokens; };
+  auto block_of = [&](int k) {
+    int blk = __builtin_amdgcn_readlane(ent, min(k, my_blocks - 1));
+    return ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
+  };
+  auto load_block = [&](typename Policy::Frag& fr, int k) {
+    const bool real = k < my_blocks;
+    const int blk = block_of(k);
+    k = min(k, my_blocks - 1);
+    const int rows = min(kBlockTokens, t_end - tok_of(k));
+    const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
+    const size_t o = (size_t)blk * block_bytes;
+    pol.load(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
+  };
+  auto is_new = [&](int k) { return FUSED && block_of(k) == blk_new; };
   if (my_blocks > 0) {
-    // NPF fragments in rotation: the loads of the next NPF-1 blocks are in
-    // flight while a block is computed, and no register copy of in-flight
-    // data is ever needed (the rotation is unrolled, so every fragment index
-    // is static). Each block is read through a buffer descriptor covering
-    // only its rows that hold context tokens, so rows past the context (any
-    // bits, NaN included) read as zeros. Steps past the last block issue their
-    // loads through an empty descriptor: they return zeros without touching
-    // memory, which keeps the load count of every step the same.
-    typename Policy::Frag f[NPF];
-    auto tok_of = [&](int k) { return (b_begin + wave + k * W) * kBlockTokens; };
-    auto block_of = [&](int k) {
-      int blk = __builtin_amdgcn_readlane(ent, min(k, my_blocks - 1));
-      return ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
-    };
-    auto load_block = [&](typename Policy::Frag& fr, int k) {
-      const bool real = k < my_blocks;
-      const int blk = block_of(k);
-      k = min(k, my_blocks - 1);
-      const int rows = min(kBlockTokens, t_end - tok_of(k));
-      const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
-      const size_t o = (size_t)blk * block_bytes;
-      pol.load(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
-    };
-    auto is_new = [&](int k) { return FUSED && block_of(k) == blk_new; };
 #pragma unroll
     for (int j = 0; j < NPF - 1; ++j) load_block(f[j], j);
+  }
+  if constexpr (FUSED) __syncthreads();  // the new row is in LDS before any block needs it
+  if (my_blocks > 0) {
     for (int k0 = 0;; k0 += NPF) {
 #pragma unroll
       for (int j = 0; j < NPF; ++j) {
         const int k = k0 + j;
         load_block(f[(j + NPF - 1) % NPF], k + NPF - 1);
-        pol.process(f[j], tok_of(k), t_end, sh.scale_log2, is_new(k));
+        pol.process(f[j], tok_of(k), t_end, sh.scale_log2, is_new(k), sm_nk, sm_nv);
         if (k + 1 >= my_blocks) goto blocks_done;
       }
     }
   blocks_done:;
   }
   if constexpr (FUSED) {
-    if (writer) pol.store_new_row(k_cache + new_dst, v_cache + new_dst);
+    if (writer && lane < D / 8) {   // the store of record
+      *(uint4*)(k_cache + new_dst + lane * 8) = sm_nk[lane];
+      *(uint4*)(v_cache + new_dst + lane * 8) = sm_nv[lane];
+    }
   }
   pol.to_lds(sm_m[wave], sm_l[wave], sm_o[wave]);
   __syncthreads();
@@ -585,8 +578,17 @@ __device__ __forceinline__ void decode_item(
 // Work-list mode: grid (X, Hkv); the plan kernel has written the count and
 // the (sequence, partition) items of all non-empty partitions, and workgroup
 // x takes items x, x+X, ... so no workgroup is launched for nothing.
+// Waves per SIMD the register allocation must allow. Four (<= 128 VGPRs)
+// keep every workgroup of a 1024-workgroup grid of 4-wave groups resident
+// at once: at 129 VGPRs the TinyLlama-shaped grid ran a quarter of its
+// workgroups as a late second round (79 us instead of 67). The D = 128
+// kernels with g >= 2 would spill at 128 and take two (the compiler then
+// settles at three for VALU, two for MFMA).
+template <int D, int G>
+constexpr int kMinWavesPerSimd = (D == 64 || G == 1) ? 4 : 2;
+
 template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void paged_decode_partition_kernel(
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<D, G>))) void paged_decode_partition_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
     uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -597,6 +599,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   __shared__ float sm_m[W][G];
   __shared__ float sm_l[W][G];
   __shared__ int sm_last;
+  __shared__ uint4 sm_new[2][D / 8];  // the step's new K and V row (fused write)
   if (items == nullptr) {
     // Workgroups are dealt round-robin to the 8 XCDs in dispatch order; remap
     // so that each XCD runs a contiguous range of (sequence fastest, then KV
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
                                                block_tables, context_lens, sh, new_key,
                                                new_value, slots, counters, sm_o, sm_m, sm_l,
-                                               &sm_last);
+                                               &sm_last, sm_new[0], sm_new[1]);
     return;
   }
   const int count = items[0];
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache,
                                                v_cache, block_tables, context_lens, sh, new_key,
                                                new_value, slots, counters, sm_o, sm_m, sm_l,
-                                               &sm_last);
+                                               &sm_last, sm_new[0], sm_new[1]);
     __syncthreads();  // the LDS of this item is read before the next item writes it
   }
 }
