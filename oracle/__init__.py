@@ -1,4 +1,5 @@
-"""CPU float64 oracle for paged-attention decode and the paged cache write.
+"""CPU float64 oracle for paged-attention decode (one or several new tokens per
+sequence) and the paged cache write.
 
 TEST INFRASTRUCTURE ONLY: imported by `tests/`, `__graft_entry__.smoke()` and
 the `cpu_baseline` leg of `bench.py`, never by the product path. It shares no
@@ -14,6 +15,7 @@ from .paged_attention import (  # noqa: F401
     gather_sequence,
     paged_decode,
     paged_decode_partitioned,
+    paged_multi_query,
     round_to_storage,
     widen,
 )

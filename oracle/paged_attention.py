@@ -24,6 +24,15 @@ What is computed, and where it comes from:
 * GQA grouping (not named by the pages; the plainest reading that matches the
   Hugging Face grouping the write-up's parity tests are anchored to, section
   "HF一致性作为正确性锚点"): query head j reads KV head `j // (Hq // Hkv)`.
+* Several new tokens per sequence (multi-query): the target model of
+  speculative decoding scores the last accepted token and K draft tokens in
+  one forward pass ("从零手写 vLLM 核心：mini-vllm 项目深度解析", section
+  "推测解码原理"; its "工程启示" section notes the KV-rollback machinery this
+  needs), and a prefill chunk appended to a cached prefix is the same shape.
+  The n new tokens of a sequence are the last n of its `context_lens[s]`
+  cached tokens (their K/V rows are in the pools), and new token i, at
+  position L - n + i, attends causally over positions 0..L - n + i: exact
+  softmax attention over that prefix, in float64.
 * Cache write: new token i's K/V row goes to flat slot `slot_mapping[i]`,
   i.e. block `slot // block_size`, offset `slot % block_size`; negative slots
   are padding and are skipped. This is a raw copy, so it is bit-exact.
@@ -46,6 +55,7 @@ __all__ = [
     "gather_sequence",
     "paged_decode",
     "paged_decode_partitioned",
+    "paged_multi_query",
     "round_to_storage",
 ]
 
@@ -215,4 +225,52 @@ def paged_decode_partitioned(q, k_cache, v_cache, block_tables, context_lens, sc
             big_m = max(ms)
             w = np.array([l * math.exp(m - big_m) for m, l in zip(ms, ls)])
             out[s, j] = (w[:, None] * np.array(os_)).sum(axis=0) / w.sum()
+    return out
+
+
+def paged_multi_query(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                      block_tables: np.ndarray, context_lens: np.ndarray,
+                      query_start: np.ndarray, scale: float, dtype: str,
+                      block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """Exact causal attention of several new query tokens per sequence, float64.
+
+    Sequence s owns query rows query_start[s] .. query_start[s+1]-1 of q
+    (`[T, Hq, D]` raw bits, T = query_start[S]); they are its n_s newest
+    tokens, the last n_s of its context_lens[s] = L_s cached tokens. Row
+    query_start[s] + i holds the token at position L_s - n_s + i, which
+    attends over positions 0 .. L_s - n_s + i. A sequence with n_s = 0 has no
+    rows; n_s > L_s is invalid. Returns float64 `[T, Hq, D]`.
+    """
+    block_tables = np.asarray(block_tables)
+    context_lens = np.asarray(context_lens)
+    query_start = np.asarray(query_start, dtype=np.int64)
+    S = context_lens.shape[0]
+    T, Hq, D = q.shape
+    NB, BS, Hkv, D2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or BS != block_size or D2 != D or Hq % Hkv:
+        raise ValueError("pool layout does not match q / block_size / head counts")
+    if block_tables.shape[0] != S or query_start.shape[0] != S + 1 or query_start[0] != 0 \
+            or query_start[S] != T or np.any(np.diff(query_start) < 0):
+        raise ValueError("query_start must run from 0 to T without decreasing, one entry per sequence + 1")
+    group = Hq // Hkv
+    qf = widen(q, dtype)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in range(S):
+        length = int(context_lens[s])
+        first, n_new = int(query_start[s]), int(query_start[s + 1] - query_start[s])
+        if n_new == 0:
+            continue
+        if n_new > length:
+            raise ValueError(f"sequence {s}: {n_new} new tokens but only {length} in its context")
+        ks = widen(gather_sequence(k_cache, block_tables[s], length, block_size), dtype)
+        vs = widen(gather_sequence(v_cache, block_tables[s], length, block_size), dtype)
+        for i in range(n_new):
+            row = first + i
+            visible = length - n_new + i + 1      # positions 0 .. L - n + i
+            for j in range(Hq):
+                h = j // group
+                z = scale * (ks[:visible, h, :] @ qf[row, j])
+                z = z - z.max()
+                e = np.exp(z)
+                out[row, j] = (e / e.sum()) @ vs[:visible, h, :]
     return out

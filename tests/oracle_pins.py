@@ -1,7 +1,8 @@
 """Pins for the CPU oracle: checks against things other than the oracle itself.
 
 Each `pin_*` takes an oracle-like module `o` (attributes `paged_decode`,
-`paged_decode_partitioned`, `cache_write`, `widen`) and raises AssertionError
+`paged_decode_partitioned`, `paged_multi_query`, `cache_write`, `widen`) and
+raises AssertionError
 (or any exception) when the oracle disagrees with:
 
 * hand-derived closed-form cases (tests/golden/closed_form_decode.json,
@@ -339,6 +340,103 @@ def pin_large_logits_finite(o):
         ref = attend_contiguous(c["qf"][s].tolist(), c["k_seq"][s].tolist(),
                                 c["v_seq"][s].tolist(), 400.0, 1)
         assert np.allclose(got[s], np.array(ref), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------- several new tokens per sequence
+
+def mq_case(rng, dtype, lens, news, hq, hkv, d, extra_blocks=3):
+    """A paged case plus query rows for `news[s]` new tokens per sequence."""
+    c = random_case(rng, dtype, lens, hq, hkv, d, extra_blocks)
+    qf = random_dyadic(rng, (sum(news), hq, d))
+    c.update(mq_qf=qf, mq_q=bits_of(qf, dtype), news=list(news),
+             qstart=np.concatenate([[0], np.cumsum(news)]).astype(np.int32))
+    return c
+
+
+def run_mq(o, c, scale):
+    return o.paged_multi_query(c["mq_q"], c["kp"], c["vp"], c["tables"], c["lens"], c["qstart"],
+                               scale, c["dtype"])
+
+
+def mq_rows(c):
+    """(sequence, new-token index, q row, visible prefix length) of every row."""
+    for s, n in enumerate(c["news"]):
+        for i in range(n):
+            yield s, i, int(c["qstart"][s]) + i, int(c["lens"][s]) - n + i + 1
+
+
+def pin_mq_bruteforce(o):
+    rng = np.random.default_rng(20)
+    for dtype, lens, news, hq, hkv, d in (("f16", [1, 17, 40, 9, 33], [1, 5, 3, 0, 33], 4, 2, 8),
+                                          ("bf16", [16, 30], [16, 2], 8, 1, 4)):
+        c = mq_case(rng, dtype, lens, news, hq, hkv, d)
+        got = run_mq(o, c, 0.41)
+        assert got.shape == (sum(news), hq, d)
+        for s, i, row, vis in mq_rows(c):
+            ref = attend_contiguous(c["mq_qf"][row].tolist(), c["k_seq"][s][:vis].tolist(),
+                                    c["v_seq"][s][:vis].tolist(), 0.41, hkv)
+            assert np.allclose(got[row], np.array(ref), rtol=0, atol=1e-12), (dtype, s, i)
+
+
+def pin_mq_torch_sdpa_causal(o):
+    """torch's attention with an explicit mask over contiguous K/V: new token i
+    of a sequence with L cached tokens, n of them new, sees t <= L - n + i."""
+    import torch
+    rng = np.random.default_rng(21)
+    lens, news, g = [45, 7, 20], [4, 7, 1], 4
+    c = mq_case(rng, "bf16", lens, news, 8, 2, 16)
+    got = run_mq(o, c, 0.25)
+    for s, (L, n) in enumerate(zip(lens, news)):
+        k = torch.tensor(np.repeat(c["k_seq"][s], g, axis=1)).permute(1, 0, 2)   # [Hq, L, D]
+        v = torch.tensor(np.repeat(c["v_seq"][s], g, axis=1)).permute(1, 0, 2)
+        r0 = int(c["qstart"][s])
+        q = torch.tensor(c["mq_qf"][r0:r0 + n]).permute(1, 0, 2)                  # [Hq, n, D]
+        mask = torch.arange(L)[None, :] <= (L - n + torch.arange(n))[:, None]     # [n, L]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=0.25)
+        assert np.allclose(got[r0:r0 + n], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12), s
+
+
+def pin_mq_zero_query_is_prefix_mean(o):
+    rng = np.random.default_rng(22)
+    c = mq_case(rng, "f16", [12, 40], [6, 3], 2, 1, 4)
+    c["mq_q"] = bits_of(np.zeros_like(c["mq_qf"]), "f16")
+    got = run_mq(o, c, 1.0)
+    for s, i, row, vis in mq_rows(c):
+        vs = c["v_seq"][s][:vis, 0]
+        mean = [math.fsum(vs[:, e]) / vis for e in range(4)]
+        for j in range(2):
+            assert np.allclose(got[row, j], mean, rtol=0, atol=1e-12), (s, i)
+
+
+def pin_mq_first_prefill_token_returns_v0(o):
+    """A sequence whose whole context is new: its first token sees only itself."""
+    rng = np.random.default_rng(23)
+    c = mq_case(rng, "bf16", [21, 5], [21, 5], 4, 2, 8)
+    got = run_mq(o, c, 2.0)
+    for s in range(2):
+        row = int(c["qstart"][s])
+        for j in range(4):
+            assert np.array_equal(got[row, j], c["v_seq"][s][0, j // 2]), (s, j)
+
+
+def pin_mq_one_new_token_is_decode(o):
+    rng = np.random.default_rng(24)
+    c = mq_case(rng, "f16", [1, 30, 64, 17], [1, 1, 1, 1], 8, 2, 8)
+    got = run_mq(o, c, 0.7)
+    ref = o.paged_decode(c["mq_q"], c["kp"], c["vp"], c["tables"], c["lens"], 0.7, "f16")
+    assert np.allclose(got, ref, rtol=0, atol=1e-13)
+
+
+def pin_mq_permutation_invariance(o):
+    rng = np.random.default_rng(25)
+    c = mq_case(rng, "bf16", [33, 9, 50], [4, 9, 2], 4, 2, 8, extra_blocks=6)
+    ref = run_mq(o, c, 0.5)
+    pi = rng.permutation(c["kp"].shape[0])
+    kp2, vp2 = np.empty_like(c["kp"]), np.empty_like(c["vp"])
+    kp2[pi], vp2[pi] = c["kp"], c["vp"]
+    t2 = np.where(c["tables"] >= 0, pi[np.maximum(c["tables"], 0)], -1).astype(np.int32)
+    got = o.paged_multi_query(c["mq_q"], kp2, vp2, t2, c["lens"], c["qstart"], 0.5, "bf16")
+    assert np.array_equal(got, ref)
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

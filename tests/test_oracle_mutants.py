@@ -25,6 +25,10 @@ MUTANTS = {
     "cache_slot_divmod_swapped": ("blk, off = divmod(int(slot), block_size)",
                                   "off, blk = divmod(int(slot), block_size)"),
     "cache_negative_not_skipped": ("if slot < 0:\n            continue", "if False:\n            continue"),
+    "mq_no_causal_mask": ("visible = length - n_new + i + 1", "visible = length"),
+    "mq_causal_off_by_one": ("visible = length - n_new + i + 1", "visible = length - n_new + i + 2"),
+    "mq_positions_from_start": ("visible = length - n_new + i + 1", "visible = i + 1"),
+    "mq_query_rows_reversed": ("row = first + i\n", "row = first + n_new - 1 - i\n"),
     "length_ignores_last_token": ("length = int(context_lens[s])\n        if length <= 0:\n            weights",
                                   "length = int(context_lens[s]) - 1\n        if length <= 0:\n            weights"),
 }
