@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MVK_ABI_VERSION 2
+#define MVK_ABI_VERSION 3
 
 typedef enum mvk_status {
     MVK_OK = 0,
@@ -190,6 +190,72 @@ int32_t mvk_paged_attention_decode(void* out, const void* q,
                                    int32_t max_blocks_per_seq, int32_t max_context_len,
                                    float scale, int32_t dtype, int32_t partition_tokens,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mvk_paged_attention_multi_query_workspace_size - bytes of scratch that
+ * mvk_paged_attention_multi_query needs for these sizes (0 when no sequence
+ * is split into partitions), and the partition length it will use.
+ * Arguments as for mvk_paged_attention_multi_query. Errors: as for its size
+ * checks.
+ */
+int32_t mvk_paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_query_tokens,
+                                                       int32_t max_query_len, int32_t num_q_heads,
+                                                       int32_t num_kv_heads, int32_t head_dim,
+                                                       int32_t max_context_len,
+                                                       int32_t partition_tokens,
+                                                       size_t* workspace_bytes,
+                                                       int32_t* chosen_partition_tokens);
+
+/*
+ * mvk_paged_attention_multi_query - paged attention for several new tokens
+ * per sequence, causal among them: the target model's verification pass of
+ * speculative decoding, which scores the last accepted token and K draft
+ * tokens in one forward pass ("从零手写 vLLM 核心：mini-vllm 项目深度解析",
+ * section "推测解码原理"), and a short prefill chunk over a cached prefix.
+ *
+ * Defines, for sequence s with L = context_lens[s] cached tokens of which the
+ * last n = query_start[s+1] - query_start[s] are new (their K/V rows already
+ * in the pools, e.g. written by mvk_reshape_and_cache), for new token
+ * i < n (query row t = query_start[s] + i, position L - n + i), query head j
+ * and h = j / g:
+ *   out[t][j] = sum_{u <= L-n+i} softmax_u(scale * q[t][j] . K_u[h]) V_u[h]
+ * Arithmetic, rounding, block addressing and GQA grouping are those of
+ * mvk_paged_attention_decode; with n = 1 for every sequence the result equals
+ * the decode call's.
+ *
+ *   out, q        [num_query_tokens, num_q_heads, head_dim], dtype; out written.
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim], dtype; read.
+ *   v_cache
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq] (as for decode).
+ *   context_lens  int32 [num_seqs]; each <= max_context_len, and >= its n.
+ *   query_start   int32 [num_seqs + 1], on the device: 0 = query_start[0] <=
+ *                 ... <= query_start[num_seqs] = num_query_tokens; every
+ *                 n <= max_query_len and n <= L. A sequence with n = 0 has
+ *                 no rows. (n > L is not checked on the device: such rows see
+ *                 only the positions that exist, or none, and are then zero.)
+ *   max_query_len host-side bound of n, in [1, 1024].
+ *   max_context_len, scale, dtype, partition_tokens: as for decode.
+ *   workspace     device scratch of workspace_bytes (from the query above with
+ *                 the same sizes); may be NULL when that size is 0; owned by
+ *                 the caller, needs no clearing, not shared by concurrent calls.
+ *   head_dim 64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
+ *   block_size 16. num_seqs == 0 or num_query_tokens == 0 is a no-op.
+ * Unread pool slots may hold any bits. Repeated calls give identical bits.
+ * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED,
+ * MVK_ERR_WORKSPACE_TOO_SMALL, MVK_ERR_HIP.
+ */
+int32_t mvk_paged_attention_multi_query(void* out, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables,
+                                        const int32_t* context_lens,
+                                        const int32_t* query_start,
+                                        int32_t num_seqs, int32_t num_query_tokens,
+                                        int32_t max_query_len, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t num_blocks,
+                                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                                        float scale, int32_t dtype, int32_t partition_tokens,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,10 @@ is no fallback: if libmvk.so is missing, the first call fails with instructions.
                            max_context_len=None, out=None, partition_tokens=0,
                            workspace=None, new_key=None, new_value=None,
                            slot_mapping=None)
+    paged_attention_multi_query(q, k_cache, v_cache, block_tables, context_lens,
+                                query_start, scale, max_query_len=None,
+                                max_context_len=None, out=None, partition_tokens=0,
+                                workspace=None)
 
 The loader relies on torch having loaded its HIP runtime first: the library's
 dependency on libamdhip64.so.7 then resolves to that same runtime, so the
@@ -24,7 +28,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmvk.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MVK_OK = 0
 MVK_ERR_INVALID_ARGUMENT = 1
 MVK_ERR_UNSUPPORTED = 2
@@ -49,6 +53,13 @@ SIGNATURES = {
                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int, _c_int, _c_float, _c_int, _c_int, _ptr,
                                             _c_size, _ptr]),
+    "mvk_paged_attention_multi_query_workspace_size": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                 ctypes.POINTER(_c_size), ctypes.POINTER(_c_int)]),
+    "mvk_paged_attention_multi_query": (
+        _c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
+                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _ptr, _c_size,
+                 _ptr]),
 }
 
 
@@ -222,3 +233,73 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                           ws_bytes, _stream(q.device))
     _check("mvk_paged_attention_decode", st)
     return out
+
+
+def multi_query_workspace_size(num_seqs: int, num_query_tokens: int, max_query_len: int,
+                               num_q_heads: int, num_kv_heads: int, head_dim: int,
+                               max_context_len: int, partition_tokens: int = 0):
+    """(workspace bytes, partition length) the multi-query call will use."""
+    nbytes = ctypes.c_size_t(0)
+    chosen = ctypes.c_int32(0)
+    st = lib().mvk_paged_attention_multi_query_workspace_size(
+        num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
+        max_context_len, partition_tokens, ctypes.byref(nbytes), ctypes.byref(chosen))
+    _check("mvk_paged_attention_multi_query_workspace_size", st)
+    return nbytes.value, chosen.value
+
+
+def paged_attention_multi_query(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                query_start: torch.Tensor, scale: float,
+                                max_query_len: int | None = None,
+                                max_context_len: int | None = None,
+                                out: torch.Tensor | None = None, partition_tokens: int = 0,
+                                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Several new tokens per sequence, causal among them: sequence s owns
+    query rows query_start[s] .. query_start[s+1]-1 of q ([T, Hq, D]), the
+    last n_s of its context_lens[s] cached tokens; row query_start[s] + i
+    attends over positions 0 .. context_lens[s] - n_s + i.
+
+    `max_query_len` / `max_context_len` must bound n_s / context_lens; when
+    omitted they are read from the device (a synchronising copy). The
+    workspace (uint8, on the device, at least multi_query_workspace_size()
+    bytes) needs no clearing; it is allocated through torch when needed and
+    not given."""
+    _require(q, "q", ndim=3)
+    _require(k_cache, "k_cache", dtype=q.dtype, ndim=4)
+    _require(v_cache, "v_cache", dtype=q.dtype, ndim=4)
+    _require(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _require(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _require(query_start, "query_start", dtype=torch.int32, ndim=1)
+    T, hq, d = q.shape
+    S = context_lens.shape[0]
+    nb, bs, hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d or block_tables.shape[0] != S \
+            or query_start.shape[0] != S + 1:
+        raise ValueError("inconsistent shapes")
+    if max_query_len is None:
+        max_query_len = max(int((query_start[1:] - query_start[:-1]).max().item()), 1) if S else 1
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if S else 0
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", dtype=q.dtype)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    need, _ = multi_query_workspace_size(S, T, max_query_len, hq, hkv, d, max_context_len,
+                                         partition_tokens)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _require(workspace, "workspace", dtype=torch.uint8)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib().mvk_paged_attention_multi_query(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), S, T,
+        max_query_len, hq, hkv, d, bs, nb, block_tables.shape[1], max_context_len, float(scale),
+        _dtype_code(q), partition_tokens, ws_ptr, ws_bytes, _stream(q.device))
+    _check("mvk_paged_attention_multi_query", st)
+    return out
+

@@ -125,6 +125,61 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   return MVK_OK;
 }
 
+// ------------------------------------------------ multi-query (several new tokens)
+
+// Query tokens per sequence that one call accepts: verification of K draft
+// tokens and short prefill chunks. Longer chunks are prefill's job.
+constexpr int32_t kMaxQueryLen = 1024;
+constexpr int32_t kMqRowTile = 16;  // (new token, query head) rows per workgroup
+
+struct MqPlan {
+  int32_t partition_tokens;
+  int32_t num_parts;
+  int32_t waves;
+  int32_t row_groups;      // row tiles per (sequence, KV head)
+  size_t workspace_bytes;  // partial (m, l, o) states, when sequences are split
+};
+
+int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_context_len, int32_t partition_tokens, MqPlan* plan) {
+  if (num_seqs < 0 || num_query_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_context_len < 0 || max_query_len < 1 || max_query_len > kMaxQueryLen)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return MVK_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_query_tokens > (int64_t)num_seqs * max_query_len)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (partition_tokens != 0 &&
+      (partition_tokens < kBlock || partition_tokens > kMaxPartition || partition_tokens % kBlock))
+    return MVK_ERR_INVALID_ARGUMENT;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!mvk::decode_supported(head_dim, group)) return MVK_ERR_UNSUPPORTED;
+  const int32_t row_groups = (max_query_len * group + kMqRowTile - 1) / kMqRowTile;
+  const int64_t units = (int64_t)num_seqs * row_groups;  // workgroups per KV head and partition
+  int32_t p = partition_tokens
+                  ? partition_tokens
+                  : default_partition((int32_t)(units < INT32_MAX ? units : INT32_MAX),
+                                      num_kv_heads, max_context_len);
+  int32_t waves = default_waves(p);
+#ifdef MVK_TUNING
+  if (!partition_tokens && getenv("MVK_TUNE_P")) p = atoi(getenv("MVK_TUNE_P"));
+  if (getenv("MVK_TUNE_W")) waves = atoi(getenv("MVK_TUNE_W"));
+  if (p < kBlock || p > kMaxPartition || p % kBlock || (waves != 4 && waves != 8))
+    return MVK_ERR_INVALID_ARGUMENT;
+#endif
+  int64_t parts = ((int64_t)max_context_len + p - 1) / p;
+  if (parts < 1) parts = 1;
+  if (units * num_kv_heads * parts > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;  // 1-D grid
+  plan->partition_tokens = p;
+  plan->num_parts = (int32_t)parts;
+  plan->waves = waves;
+  plan->row_groups = row_groups;
+  plan->workspace_bytes = parts > 1 ? (size_t)num_query_tokens * num_q_heads * (size_t)parts *
+                                          (size_t)(head_dim + 2) * 4u
+                                    : 0;
+  return MVK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,6 +303,81 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;
   hipError_t err = mvk::launch_paged_decode(a, (hipStream_t)stream);
+  return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
+}
+
+int32_t mvk_paged_attention_multi_query_workspace_size(
+    int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len, int32_t partition_tokens,
+    size_t* workspace_bytes, int32_t* chosen_partition_tokens) {
+  if (!workspace_bytes) return MVK_ERR_INVALID_ARGUMENT;
+  MqPlan plan;
+  const int32_t st = check_mq_sizes(num_seqs, num_query_tokens, max_query_len, num_q_heads,
+                                    num_kv_heads, head_dim, max_context_len, partition_tokens,
+                                    &plan);
+  if (st != MVK_OK) return st;
+  *workspace_bytes = plan.workspace_bytes;
+  if (chosen_partition_tokens) *chosen_partition_tokens = plan.partition_tokens;
+  return MVK_OK;
+}
+
+int32_t mvk_paged_attention_multi_query(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+    int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != MVK_F16 && dtype != MVK_BF16) return MVK_ERR_INVALID_ARGUMENT;
+  if (block_size != kBlock) return MVK_ERR_UNSUPPORTED;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale))
+    return MVK_ERR_INVALID_ARGUMENT;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+    return MVK_ERR_INVALID_ARGUMENT;
+  MqPlan plan;
+  const int32_t st = check_mq_sizes(num_seqs, num_query_tokens, max_query_len, num_q_heads,
+                                    num_kv_heads, head_dim, max_context_len, partition_tokens,
+                                    &plan);
+  if (st != MVK_OK) return st;
+  if (num_seqs == 0 || num_query_tokens == 0) return MVK_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(query_start))
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (out == q || out == k_cache || out == v_cache || k_cache == v_cache)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return MVK_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return MVK_ERR_INVALID_ARGUMENT;
+  }
+
+  mvk::MultiQueryArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  const size_t n_state = (size_t)num_query_tokens * num_q_heads * (size_t)plan.num_parts;
+  a.ws_ml = plan.workspace_bytes ? (float*)workspace : nullptr;
+  a.ws_o = plan.workspace_bytes ? (float*)workspace + n_state * 2 : nullptr;
+  a.num_seqs = num_seqs;
+  a.max_query_len = max_query_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.partition_tokens = plan.partition_tokens;
+  a.num_parts = plan.num_parts;
+  a.row_groups = plan.row_groups;
+  a.waves = plan.waves;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  a.dtype = dtype;
+  hipError_t err = mvk::launch_paged_multi_query(a, (hipStream_t)stream);
   return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
 }
 

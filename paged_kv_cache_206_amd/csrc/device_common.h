@@ -7,6 +7,15 @@
 namespace mvk {
 
 constexpr int kBlockTokens = 16;  // tokens per KV block
+constexpr uint32_t kXcds = 8;     // accelerator complex dies of an MI355X
+
+// Workgroups are dealt round-robin to the 8 XCDs in dispatch order. Dispatch
+// index i of n maps to the item index returned here, so that each XCD runs a
+// contiguous range of items (and items that read the same data share an L2).
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t i, uint32_t n) {
+  const uint32_t xcd = i % kXcds, per = n / kXcds, rem = n % kXcds;
+  return xcd * per + min(xcd, rem) + i / kXcds;
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));

@@ -42,4 +42,25 @@ bool decode_supported(int32_t head_dim, int32_t group);
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
+struct MultiQueryArgs {
+  void* out;                   // [T, Hq, D]
+  const void* q;               // [T, Hq, D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;  // [S + 1]: sequence s owns query rows [query_start[s], query_start[s+1])
+  float* ws_ml;  // [T, Hq, num_parts, 2] (running max in log2 units, denominator)
+  float* ws_o;   // [T, Hq, num_parts, D] normalised partial outputs
+  int32_t num_seqs, max_query_len, num_q_heads, num_kv_heads, head_dim;
+  int32_t num_blocks, max_blocks_per_seq, max_context_len;
+  int32_t partition_tokens, num_parts;
+  int32_t row_groups;  // groups of 16 (new token, query head) rows per (sequence, KV head)
+  int32_t waves;       // waves per workgroup (4 or 8)
+  float scale_log2;
+  int32_t dtype;
+};
+
+hipError_t launch_paged_multi_query(const MultiQueryArgs& a, hipStream_t stream);
+
 }  // namespace mvk

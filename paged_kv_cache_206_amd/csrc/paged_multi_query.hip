@@ -1,0 +1,292 @@
+// Multi-query paged attention for gfx950 (CDNA4), wave64: each sequence
+// brings n_s >= 1 new query tokens, the last n_s of its context_lens[s] = L
+// cached tokens, and new token i (position L - n_s + i) attends causally over
+// positions 0 .. L - n_s + i.
+//
+// Method ("从零手写 vLLM 核心：mini-vllm 项目深度解析", section "推测解码原理"):
+// the target model of speculative decoding scores the last accepted token and
+// K draft tokens of every sequence in one forward pass; a prefill chunk
+// appended to a cached prefix has the same shape. The cache is the paged one
+// of the decode kernel (same page, "2. 分页KV缓存（PagedAttention）" and
+// "关键工程决策" item 3): 16-token blocks of separate K/V pools
+// [num_blocks, 16, Hkv, D] found through per-sequence block tables.
+//
+// Work decomposition: the n_s * g rows of a (sequence, KV head) - row i*g + j
+// is new token i with query head j of the group - are cut into groups of 16
+// rows, one MFMA tile (attention_mfma.h). One workgroup per (row group,
+// sequence, KV head, partition); the partition's blocks are dealt round-robin
+// to its W waves, which stream them two at a time as in decode. Row groups of
+// the same (sequence, KV head, partition) read the same blocks and are
+// adjacent in the XCD-contiguous order, so after the first they read them
+// from the XCD's L2. Each row carries its own causal limit, so rows of one
+// tile see different numbers of tokens of the same block.
+//
+// Long contexts: partial (m, l, o) states per (query row, partition) go to
+// the workspace and a second kernel merges them with the log-sum-exp rule
+// in partition order.
+#include "attention_mfma.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace mvk {
+
+namespace {
+
+constexpr int kMqRows = 16;      // query rows per workgroup: one MFMA tile
+constexpr int kMqPrefetch = 2;   // blocks whose loads are in flight per wave
+constexpr int kMqMergeThreads = 256;
+
+struct MqShape {
+  int32_t num_seqs, num_kv_heads, num_blocks, max_blocks, max_context_len, max_query_len;
+  int32_t partition_tokens, num_parts, row_groups;
+  float scale_log2;
+};
+
+// A work item, from the XCD-contiguous item index: row group fastest, then
+// sequence, KV head, partition.
+struct MqItem {
+  int rg, s, h, part;
+};
+
+__device__ __forceinline__ MqItem mq_item(uint32_t v, const MqShape& sh) {
+  MqItem it;
+  it.rg = v % sh.row_groups;
+  v /= sh.row_groups;
+  it.s = v % sh.num_seqs;
+  v /= sh.num_seqs;
+  it.h = v % sh.num_kv_heads;
+  it.part = v / sh.num_kv_heads;
+  return it;
+}
+
+// Query row r of a (sequence, KV head) with n new tokens is new token r / G,
+// query head h*G + r % G: its index in the [T, Hq] row space.
+template <int G>
+__device__ __forceinline__ size_t mq_out_row(int first_token, int r, int h, int Hq) {
+  return (size_t)(first_token + r / G) * Hq + (size_t)h * G + r % G;
+}
+
+// Two waves per SIMD for D = 128 (the MFMA tile needs about 190 registers),
+// four for D = 64.
+template <int D>
+constexpr int kMqMinWavesPerSimd = D == 64 ? 4 : 2;
+
+template <int DT, int D, int G, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMqMinWavesPerSimd<D>)))
+void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
+                               float* __restrict__ ws_o, const uint16_t* __restrict__ q,
+                               const uint16_t* __restrict__ k_cache,
+                               const uint16_t* __restrict__ v_cache,
+                               const int32_t* __restrict__ block_tables,
+                               const int32_t* __restrict__ context_lens,
+                               const int32_t* __restrict__ query_start, MqShape sh) {
+  using Policy = MfmaPolicy<DT, D, kMqRows>;
+  using E = Elem<DT>;
+  constexpr int NPF = kMqPrefetch;
+  __shared__ float sm_o[W][kMqRows * D];
+  __shared__ float sm_m[W][kMqRows];
+  __shared__ float sm_l[W][kMqRows];
+
+  const MqItem it = mq_item(xcd_contiguous(blockIdx.x, gridDim.x), sh);
+  const int s = it.s, h = it.h, part = it.part;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int Hq = sh.num_kv_heads * G;
+  const int P = sh.partition_tokens;
+  const int t_begin = part * P;
+  const int b_begin = t_begin / kBlockTokens;
+
+  // Prologue: context length, query range and this wave's table entries
+  // (lane k <- block b_begin + wave + k*W) are fetched together.
+  const int len = context_lens[s];
+  const int first = query_start[s];
+  const int last = query_start[s + 1];
+  const int part_blocks = min(P / kBlockTokens, sh.max_blocks - b_begin);
+  const int32_t* table = block_tables + (size_t)s * sh.max_blocks;
+  int ent = 0;
+  if (wave + lane * W < part_blocks) ent = table[b_begin + wave + lane * W];
+
+  const int L = min(len, sh.max_context_len);
+  const int n_new = min(max(last - first, 0), sh.max_query_len);
+  const int rows = n_new * G;
+  const int r0 = it.rg * kMqRows;
+  if (r0 >= rows) return;  // no query rows in this group (uniform over the workgroup)
+  const int nrow = min(kMqRows, rows - r0);
+  if (t_begin >= L) {      // no context in this partition
+    if (part == 0) {       // empty context: every row is zero
+      for (int idx = threadIdx.x; idx < nrow * D; idx += W * 64)
+        out[mq_out_row<G>(first, r0 + idx / D, h, Hq) * D + idx % D] = 0;
+    }
+    return;
+  }
+  const int t_end = min(t_begin + P, L);
+  const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
+  const int my_blocks = nblk > wave ? (nblk - wave + W - 1) / W : 0;
+
+  // This lane's row slot: new token i = r / G sees tokens below L - n + i + 1.
+  const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;
+  const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
+  const int r = r0 + (lane & 15);
+  const bool valid = r < rows;
+  Policy pol;
+  pol.init_rows(valid ? q + mq_out_row<G>(first, r, h, Hq) * D : nullptr, lane, row_bytes);
+  const int row_end = valid ? min(t_end, L - n_new + r / G + 1) : 0;
+
+  const char* kbase = (const char*)(k_cache + (size_t)h * D);
+  const char* vbase = (const char*)(v_cache + (size_t)h * D);
+  if (my_blocks > 0) {
+    // The decode kernel's streaming: NPF fragments in rotation, each block
+    // read through a buffer descriptor that covers only its context rows
+    // (rows past the context read as zeros), steps past the last block
+    // issuing loads through an empty descriptor.
+    typename Policy::Frag f[NPF];
+    auto tok_of = [&](int k) { return (b_begin + wave + k * W) * kBlockTokens; };
+    auto load_block = [&](typename Policy::Frag& fr, int k) {
+      const bool real = k < my_blocks;
+      k = min(k, my_blocks - 1);
+      int blk = __builtin_amdgcn_readlane(ent, k);
+      blk = ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
+      const int nrows = min(kBlockTokens, t_end - tok_of(k));
+      const uint32_t extent = real ? (uint32_t)(nrows - 1) * row_bytes + D * 2u : 0u;
+      const size_t o = (size_t)blk * block_bytes;
+      pol.load(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
+    };
+#pragma unroll
+    for (int j = 0; j < NPF - 1; ++j) load_block(f[j], j);
+    for (int k0 = 0;; k0 += NPF) {
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        const int k = k0 + j;
+        load_block(f[(j + NPF - 1) % NPF], k + NPF - 1);
+        pol.step(f[j], tok_of(k), row_end, sh.scale_log2);
+        if (k + 1 >= my_blocks) goto blocks_done;
+      }
+    }
+  blocks_done:;
+  }
+  pol.to_lds(sm_m[wave], sm_l[wave], sm_o[wave]);
+  __syncthreads();
+
+  // Merge the waves in order; write each row, or its partial state.
+  const int parts_of_seq = (L + P - 1) / P;
+  for (int idx = threadIdx.x; idx < nrow * D; idx += W * 64) {
+    const int rl = idx / D;
+    const int d = idx % D;
+    float mm = sm_m[0][rl];
+#pragma unroll
+    for (int w = 1; w < W; ++w) mm = fmaxf(mm, sm_m[w][rl]);
+    float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float fw = fast_exp2(sm_m[w][rl] - mm);
+      lsum = fmaf(sm_l[w][rl], fw, lsum);
+      o = fmaf(sm_o[w][rl * D + d], fw, o);
+    }
+    const float res = lsum > 0.0f ? o / lsum : 0.0f;
+    const size_t orow = mq_out_row<G>(first, r0 + rl, h, Hq);
+    if (parts_of_seq == 1) {
+      out[orow * D + d] = E::round(res);
+    } else {
+      const size_t slot = orow * sh.num_parts + part;
+      ws_o[slot * D + d] = res;
+      if (d == 0) {
+        ws_ml[slot * 2] = mm;
+        ws_ml[slot * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// One workgroup per (row group, sequence, KV head) whose sequence spans
+// several partitions: out = sum_p w_p o_p / sum_p w_p with
+// w_p = l_p 2^(m_p - max m), over the partitions in index order. A partition
+// that holds none of a row's visible tokens has l_p = 0 and weighs nothing.
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
+    uint16_t* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
+    MqShape sh) {
+  using E = Elem<DT>;
+  const MqItem it = mq_item(blockIdx.x, sh);
+  const int s = it.s, h = it.h;
+  const int L = min(context_lens[s], sh.max_context_len);
+  const int P = sh.partition_tokens;
+  const int parts = (L + P - 1) / P;
+  if (parts <= 1) return;  // the partition kernel wrote these rows
+  const int first = query_start[s];
+  const int n_new = min(max(query_start[s + 1] - first, 0), sh.max_query_len);
+  const int rows = n_new * G;
+  const int r0 = it.rg * kMqRows;
+  if (r0 >= rows) return;
+  const int nrow = min(kMqRows, rows - r0);
+  const int Hq = sh.num_kv_heads * G;
+  for (int idx = threadIdx.x; idx < nrow * D; idx += kMqMergeThreads) {
+    const int d = idx % D;
+    const size_t orow = mq_out_row<G>(first, r0 + idx / D, h, Hq);
+    const float* ml = ws_ml + orow * sh.num_parts * 2;
+    const float* o = ws_o + orow * sh.num_parts * D + d;
+    float mm = -INFINITY;
+    for (int p = 0; p < parts; ++p) mm = fmaxf(mm, ml[2 * p]);
+    float acc = 0.0f, tot = 0.0f;
+    for (int p = 0; p < parts; ++p) {
+      const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - mm);
+      acc = fmaf(w, o[(size_t)p * D], acc);
+      tot += w;
+    }
+    out[orow * D + d] = E::round(tot > 0.0f ? acc / tot : 0.0f);
+  }
+}
+
+template <int DT, int D, int G, int W>
+hipError_t launch_mq_typed(const MultiQueryArgs& a, hipStream_t stream) {
+  MqShape sh{a.num_seqs,       a.num_kv_heads, a.num_blocks,       a.max_blocks_per_seq,
+             a.max_context_len, a.max_query_len, a.partition_tokens, a.num_parts,
+             a.row_groups,      a.scale_log2};
+  const int64_t items = (int64_t)a.row_groups * a.num_seqs * a.num_kv_heads * a.num_parts;
+  hipLaunchKernelGGL((paged_mq_partition_kernel<DT, D, G, W>), dim3((unsigned)items),
+                     dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                     (const uint16_t*)a.v_cache, a.block_tables, a.context_lens, a.query_start,
+                     sh);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.num_parts <= 1) return err;
+  const int64_t groups = (int64_t)a.row_groups * a.num_seqs * a.num_kv_heads;
+  hipLaunchKernelGGL((paged_mq_merge_kernel<DT, D, G>), dim3((unsigned)groups),
+                     dim3(kMqMergeThreads), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
+                     a.context_lens, a.query_start, sh);
+  return hipGetLastError();
+}
+
+template <int DT, int D, int G>
+hipError_t launch_mq_waves(const MultiQueryArgs& a, hipStream_t stream) {
+  switch (a.waves) {
+    case 4: return launch_mq_typed<DT, D, G, 4>(a, stream);
+    case 8: return launch_mq_typed<DT, D, G, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_mq_group(const MultiQueryArgs& a, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_mq_waves<DT, D, 1>(a, stream);
+    case 2: return launch_mq_waves<DT, D, 2>(a, stream);
+    case 4: return launch_mq_waves<DT, D, 4>(a, stream);
+    case 8: return launch_mq_waves<DT, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_paged_multi_query(const MultiQueryArgs& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  if (a.dtype == 0) {
+    return a.head_dim == 64 ? launch_mq_group<0, 64>(a, group, stream)
+                            : launch_mq_group<0, 128>(a, group, stream);
+  }
+  return a.head_dim == 64 ? launch_mq_group<1, 64>(a, group, stream)
+                          : launch_mq_group<1, 128>(a, group, stream);
+}
+
+}  // namespace mvk

@@ -30,7 +30,8 @@ def mvk():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "mvk_abi_version", "mvk_status_string", "mvk_reshape_and_cache",
-        "mvk_paged_attention_workspace_size", "mvk_paged_attention_decode"])
+        "mvk_paged_attention_workspace_size", "mvk_paged_attention_decode",
+        "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query"])
 
 
 def test_library_exports_every_declared_symbol(mvk):
@@ -47,7 +48,7 @@ def test_single_hip_runtime_mapped(mvk):
 
 
 def test_version_and_status_strings(mvk):
-    assert mvk.abi_version() == 2
+    assert mvk.abi_version() == 3
     assert mvk.status_string(0) == "ok"
     assert mvk.status_string(3) == "workspace too small"
     assert mvk.status_string(99) == "unknown status"
@@ -139,3 +140,55 @@ def test_workspace_size(mvk):
     assert nbytes == 65536 + 512 * 16 * parts * 130 * 4 + (1 + 2 * 512 * parts) * 4
     with pytest.raises(mvk.MvkError):
         mvk.workspace_size(2, 3, 2, 64, 10)
+
+
+def mq_call(mvk, **over):
+    a = dict(out=FAKE, q=FAKE * 2, k=FAKE * 3, v=FAKE * 4, bt=FAKE * 5, cl=FAKE * 6, qs=FAKE * 7,
+             S=4, T=12, mq=5, hq=4, hkv=2, d=64, bs=16, nb=32, mb=4, maxlen=45, scale=0.125,
+             dtype=0, part=0, ws=None, wsb=0, stream=None)
+    a.update(over)
+    return mvk.lib().mvk_paged_attention_multi_query(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["S"], a["T"], a["mq"],
+        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["maxlen"], a["scale"], a["dtype"],
+        a["part"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=2), 1),
+    (dict(bs=32), 2),
+    (dict(d=96), 2),
+    (dict(hq=6, hkv=4), 1),
+    (dict(hq=32, hkv=2), 2),
+    (dict(mq=0), 1),                  # max_query_len >= 1
+    (dict(mq=1025), 1),               # at most 1024 new tokens per sequence
+    (dict(T=21, mq=5), 1),            # more query rows than num_seqs * max_query_len
+    (dict(T=-1), 1),
+    (dict(S=-1), 1),
+    (dict(maxlen=65), 1),
+    (dict(scale=math.nan), 1),
+    (dict(part=40), 1),
+    (dict(qs=None), 1),
+    (dict(qs=FAKE * 7 + 2), 1),       # misaligned query_start
+    (dict(out=FAKE * 2), 1),          # out aliases q
+    (dict(v=FAKE * 3), 1),
+    (dict(mb=64, maxlen=1024, part=512), 3),
+    (dict(mb=64, maxlen=1024, part=512, ws=FAKE * 8, wsb=64), 3),
+])
+def test_multi_query_validation(mvk, over, status):
+    assert mq_call(mvk, **over) == status
+
+
+def test_multi_query_noop(mvk):
+    assert mq_call(mvk, S=0, T=0, out=None, q=None) == 0
+    assert mq_call(mvk, T=0, out=None, q=None) == 0
+
+
+def test_multi_query_workspace_size(mvk):
+    nbytes, p = mvk.multi_query_workspace_size(4, 12, 5, 4, 2, 64, 45)
+    assert nbytes == 0 and p >= 48
+    # 32 sequences x 5 new tokens, 32768-token contexts, 512-token partitions
+    nbytes, p = mvk.multi_query_workspace_size(32, 160, 5, 32, 8, 128, 32768, 512)
+    assert p == 512 and nbytes == 160 * 32 * 64 * (128 + 2) * 4
+    with pytest.raises(mvk.MvkError):
+        mvk.multi_query_workspace_size(2, 3, 0, 4, 2, 64, 10)
+

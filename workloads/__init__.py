@@ -188,6 +188,22 @@ def poison_unread(wl: Workload) -> None:
 
 # -------------------------------------------------------------- named configs
 
+def make_queries(wl: Workload, new_tokens, seed: int, device="cpu"):
+    """Query rows for several new tokens per sequence: sequence s gets
+    `new_tokens[s]` rows (its last new_tokens[s] context tokens). Returns
+    (q [T, Hq, D] in the workload's storage type, query_start int32 [S + 1]);
+    rows are N(0, 1) draws like the decode queries."""
+    news = torch.as_tensor(new_tokens, dtype=torch.int64)
+    if news.numel() != wl.num_seqs or bool((news < 0).any()) or \
+            bool((news > wl.context_lens.to(torch.int64)).any()):
+        raise ValueError("need 0 <= new_tokens[s] <= context_lens[s] for every sequence")
+    query_start = torch.zeros(wl.num_seqs + 1, dtype=torch.int32)
+    query_start[1:] = torch.cumsum(news, 0).to(torch.int32)
+    gen = _value_gen(seed, device)
+    q = randn_storage((int(query_start[-1]), wl.num_q_heads, wl.head_dim), wl.dtype, gen, device)
+    return q, query_start
+
+
 def make_custom(name, dtype, context_lens, num_q_heads, num_kv_heads, head_dim, num_blocks,
                 seed, layers=1, shared_prefix=None, new_rows=True, scale=None,
                 value_device="cpu", values=True) -> Workload:
