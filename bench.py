@@ -20,6 +20,12 @@ Prints ONE JSON line:
   cpu_baseline the fp64 oracle on the host, on a bounded sample of layers
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--partition P]
+                    [--new-tokens N]
+
+With --new-tokens N > 1 the step is instead, for every layer, one
+multi-query call in which each sequence brings N new tokens (the last
+accepted token and N - 1 draft tokens of speculative decoding), causal among
+them; the roofline then covers that kernel.
 """
 from __future__ import annotations
 
@@ -58,6 +64,8 @@ def parse_args():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, --steps times (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
+    ap.add_argument("--new-tokens", type=int, default=1, metavar="N",
+                    help="new tokens per sequence; N > 1 runs the multi-query kernel")
     ap.add_argument("--unfused", action="store_true",
                     help="cache write as its own call instead of fused into the decode call")
     return ap.parse_args()
@@ -94,6 +102,9 @@ def main():
     slots = wl.slot_mapping.to(dev)
     S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     maxlen = wl.max_context_len
+    if args.new_tokens > 1:
+        run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt, cl, dev)
+        return
     ws_bytes, part = mvk.workspace_size(S, Hq, Hkv, D, maxlen, args.partition)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)  # zero-filled before first use
     outs = [torch.empty_like(l.q) for l in layers]
@@ -253,6 +264,145 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def graph_time_per_call(torch, dev, calls, reps):
+    """Mean time per call of `calls` (a list of thunks) captured back to back in
+    one HIP graph, with one event pair on the stream around all replays."""
+    cur = torch.cuda.current_stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(reps):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+
+
+def run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt, cl, dev):
+    """The step with N new tokens per sequence: one multi-query call per layer."""
+    n_new = args.new_tokens
+    S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    if int(wl.context_lens.min()) < n_new:
+        raise SystemExit(f"--new-tokens {n_new} exceeds the shortest context")
+    maxlen = wl.max_context_len
+    queries = [W.make_queries(wl, [n_new] * S, seed=1000 + i, device="cuda")[0]
+               for i in range(len(layers))]
+    qs = torch.arange(0, S + 1, dtype=torch.int32, device=dev) * n_new   # query_start
+    T = S * n_new
+    ws_bytes, part = mvk.multi_query_workspace_size(S, T, n_new, Hq, Hkv, D, maxlen,
+                                                    args.partition)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(qq) for qq in queries]
+
+    def call(li):
+        l = layers[li]
+        mvk.paged_attention_multi_query(queries[li], l.k_cache, l.v_cache, bt, cl, qs, wl.scale,
+                                        max_query_len=n_new, max_context_len=maxlen,
+                                        out=outs[li], partition_tokens=part, workspace=ws)
+
+    for _ in range(max(1, args.warmup)):
+        for li in range(len(layers)):
+            call(li)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // nsets)
+    # the step (all layers) captured once and replayed; per-call time from the same graph
+    per_call_us = graph_time_per_call(torch, dev, [lambda li=li: call(li) for li in range(len(layers))],
+                                      reps)
+    ms_per_step = per_call_us * nlayers_step / 1e3
+
+    lens = wl.context_lens.to(torch.int64)
+    e = 2
+    kv_logical = int(lens.sum()) * Hkv * D * e * 2
+    kv_unique = unique_token_rows(wl) * Hkv * D * e * 2
+    alg = (kv_unique + 2 * T * Hq * D * e + int(((lens + 15) // 16).sum()) * 4 + S * 4
+           + (S + 1) * 4)
+    step_s = ms_per_step / 1e3
+    achieved = alg / (per_call_us * 1e-6) / 1e9
+    result = {
+        "metric": "paged-decode KV read GB/s (% of MI355X HBM peak); decode tokens/s",
+        "value": round(kv_logical * nlayers_step / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": reps * nsets,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "launch": "hipgraph replay of back-to-back multi-query calls",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q, random block tables)",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.workload] + f"; multi-query: {n_new} new tokens per "
+                        f"sequence (the last accepted one and {n_new - 1} drafts), causal among them",
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "block_size": 16, "layers_per_step": nlayers_step, "max_context_len": maxlen,
+            "new_tokens": n_new, "partition_tokens": part, "pool_sets": nsets,
+        },
+        "pct_hbm_peak": round(100.0 * alg * nlayers_step / step_s / 1e9 / HBM_PEAK_GBS, 2),
+        "query_tokens_per_s": round(T / step_s, 1),
+        "kv_bytes_per_step": kv_logical * nlayers_step,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_mq_partition_kernel",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(args.workload, False, kind=f"paged_multi_query_n{n_new}"),
+            "alg_bytes_per_launch": alg,
+            "launch_us": round(per_call_us, 3),
+            "launch_us_method": "hipgraph of back-to-back multi-query calls, events around the replays",
+        },
+    }
+    if not args.no_cpu and args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_multi_query(wl, layers[:nlayers_step], queries, qs,
+                                                          args.cpu_seconds, kv_logical)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_multi_query(wl, layers, queries, qs, budget_s, kv_logical_per_layer):
+    """The fp64 multi-query oracle on the host, whole layers in turn until the
+    budget is spent (at least one layer)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    bt, cl, qs_h = wl.block_tables.numpy(), wl.context_lens.numpy(), qs.cpu().numpy()
+    spent, done, hosts = 0.0, 0, {}
+    with threadpool_limits(limits=1):
+        while spent < budget_s:
+            li = done % len(layers)
+            if li not in hosts:   # host copies, untimed
+                hosts[li] = (bits(queries[li]), bits(layers[li].k_cache), bits(layers[li].v_cache))
+            qh, kc, vc = hosts[li]
+            t0 = time.perf_counter()
+            oracle.paged_multi_query(qh, kc, vc, bt, cl, qs_h, wl.scale, wl.dtype)
+            spent += time.perf_counter() - t0
+            done += 1
+    return {
+        "value": round(kv_logical_per_layer * done / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} layer passes (multi-query attention of all {wl.num_seqs} seqs; the step's "
+                  f"{len(layers)} layers in turn) until {budget_s:.0f} s were spent, numpy fp64, "
+                  f"BLAS limited to 1 thread, host copies untimed",
+        "seconds": round(spent, 3),
+        "host_cpus": os.cpu_count(),
+    }
+
+
 def kernel_source_digest():
     """sha256 over the library's kernel sources: traffic counters recorded for
     other sources are stale."""
@@ -266,13 +416,13 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(workload, fused):
-    """HBM bytes per decode call from the committed counter summary
-    (profiles/paged_decode_<workload>_hbm_traffic.md: FETCH_SIZE and WRITE_SIZE,
+def measured_traffic(workload, fused, kind="paged_decode"):
+    """HBM bytes per call from the committed counter summary
+    (profiles/<kind>_<workload>_hbm_traffic.md: FETCH_SIZE and WRITE_SIZE,
     each calibrated against a plain copy), or None when there is none for
     this kernel source."""
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", f"paged_decode_{workload}_hbm_traffic.md")
+    path = os.path.join(here, "profiles", f"{kind}_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}

@@ -136,7 +136,8 @@ struct MqPlan {
   int32_t partition_tokens;
   int32_t num_parts;
   int32_t waves;
-  int32_t row_groups;      // row tiles per (sequence, KV head)
+  int32_t tiles;           // 16-row tiles per workgroup
+  int32_t row_groups;      // workgroups per (sequence, KV head, partition)
   size_t workspace_bytes;  // partial (m, l, o) states, when sequences are split
 };
 
@@ -154,7 +155,13 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
     return MVK_ERR_INVALID_ARGUMENT;
   const int32_t group = num_q_heads / num_kv_heads;
   if (!mvk::decode_supported(head_dim, group)) return MVK_ERR_UNSUPPORTED;
-  const int32_t row_groups = (max_query_len * group + kMqRowTile - 1) / kMqRowTile;
+  // A workgroup takes up to 4 row tiles (2 with head_dim 128, whose tiles
+  // need twice the registers), so each block it loads serves all its rows.
+  const int32_t tiles_needed = (max_query_len * group + kMqRowTile - 1) / kMqRowTile;
+  const int32_t max_tiles = head_dim == 64 ? 4 : 2;
+  int32_t tiles = 1;
+  while (tiles < tiles_needed && tiles < max_tiles) tiles *= 2;
+  const int32_t row_groups = (tiles_needed + tiles - 1) / tiles;
   const int64_t units = (int64_t)num_seqs * row_groups;  // workgroups per KV head and partition
   int32_t p = partition_tokens
                   ? partition_tokens
@@ -173,6 +180,7 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
   plan->partition_tokens = p;
   plan->num_parts = (int32_t)parts;
   plan->waves = waves;
+  plan->tiles = tiles;
   plan->row_groups = row_groups;
   plan->workspace_bytes = parts > 1 ? (size_t)num_query_tokens * num_q_heads * (size_t)parts *
                                           (size_t)(head_dim + 2) * 4u
@@ -373,6 +381,7 @@ int32_t mvk_paged_attention_multi_query(
   a.max_context_len = max_context_len;
   a.partition_tokens = plan.partition_tokens;
   a.num_parts = plan.num_parts;
+  a.tiles = plan.tiles;
   a.row_groups = plan.row_groups;
   a.waves = plan.waves;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)

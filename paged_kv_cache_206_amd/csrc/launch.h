@@ -55,7 +55,8 @@ struct MultiQueryArgs {
   int32_t num_seqs, max_query_len, num_q_heads, num_kv_heads, head_dim;
   int32_t num_blocks, max_blocks_per_seq, max_context_len;
   int32_t partition_tokens, num_parts;
-  int32_t row_groups;  // groups of 16 (new token, query head) rows per (sequence, KV head)
+  int32_t tiles;       // 16-row MFMA tiles per workgroup (1, 2, or 4 with head_dim 64)
+  int32_t row_groups;  // groups of 16 * tiles (new token, query head) rows per (sequence, KV head)
   int32_t waves;       // waves per workgroup (4 or 8)
   float scale_log2;
   int32_t dtype;

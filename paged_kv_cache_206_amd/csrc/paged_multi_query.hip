@@ -12,14 +12,16 @@
 // [num_blocks, 16, Hkv, D] found through per-sequence block tables.
 //
 // Work decomposition: the n_s * g rows of a (sequence, KV head) - row i*g + j
-// is new token i with query head j of the group - are cut into groups of 16
-// rows, one MFMA tile (attention_mfma.h). One workgroup per (row group,
-// sequence, KV head, partition); the partition's blocks are dealt round-robin
-// to its W waves, which stream them two at a time as in decode. Row groups of
-// the same (sequence, KV head, partition) read the same blocks and are
-// adjacent in the XCD-contiguous order, so after the first they read them
-// from the XCD's L2. Each row carries its own causal limit, so rows of one
-// tile see different numbers of tokens of the same block.
+// is new token i with query head j of the group - are cut into tiles of 16
+// rows, one MFMA tile each (attention_mfma.h), and a workgroup takes NT tiles
+// (up to 64 rows for D = 64, 32 for D = 128), so that every block it loads
+// serves all its rows. One workgroup per (row group, sequence, KV head,
+// partition); the partition's blocks are dealt round-robin to its W waves,
+// which stream them two at a time as in decode. Row groups beyond the first
+// (more rows than one workgroup takes) read the same blocks and are adjacent
+// in the XCD-contiguous order, so they read them from the XCD's L2. Each row
+// carries its own causal limit, so rows of one tile see different numbers of
+// tokens of the same block.
 //
 // Long contexts: partial (m, l, o) states per (query row, partition) go to
 // the workspace and a second kernel merges them with the log-sum-exp rule
@@ -32,7 +34,7 @@ namespace mvk {
 
 namespace {
 
-constexpr int kMqRows = 16;      // query rows per workgroup: one MFMA tile
+constexpr int kMqRows = 16;      // query rows per MFMA tile
 constexpr int kMqPrefetch = 2;   // blocks whose loads are in flight per wave
 constexpr int kMqMergeThreads = 256;
 
@@ -66,13 +68,13 @@ __device__ __forceinline__ size_t mq_out_row(int first_token, int r, int h, int 
   return (size_t)(first_token + r / G) * Hq + (size_t)h * G + r % G;
 }
 
-// Two waves per SIMD for D = 128 (the MFMA tile needs about 190 registers),
-// four for D = 64.
-template <int D>
-constexpr int kMqMinWavesPerSimd = D == 64 ? 4 : 2;
+// Waves per SIMD the register allocation must allow: each tile's query
+// operands and accumulators take about 50 (D = 64) or 100 (D = 128) VGPRs.
+template <int D, int NT>
+constexpr int kMqMinWavesPerSimd = (D == 64 && NT == 1) ? 4 : 2;
 
-template <int DT, int D, int G, int W>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMqMinWavesPerSimd<D>)))
+template <int DT, int D, int G, int W, int NT>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMqMinWavesPerSimd<D, NT>)))
 void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                                float* __restrict__ ws_o, const uint16_t* __restrict__ q,
                                const uint16_t* __restrict__ k_cache,
@@ -109,9 +111,9 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
   const int L = min(len, sh.max_context_len);
   const int n_new = min(max(last - first, 0), sh.max_query_len);
   const int rows = n_new * G;
-  const int r0 = it.rg * kMqRows;
+  const int r0 = it.rg * (NT * kMqRows);
   if (r0 >= rows) return;  // no query rows in this group (uniform over the workgroup)
-  const int nrow = min(kMqRows, rows - r0);
+  const int nrow = min(NT * kMqRows, rows - r0);
   if (t_begin >= L) {      // no context in this partition
     if (part == 0) {       // empty context: every row is zero
       for (int idx = threadIdx.x; idx < nrow * D; idx += W * 64)
@@ -123,14 +125,19 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
   const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
   const int my_blocks = nblk > wave ? (nblk - wave + W - 1) / W : 0;
 
-  // This lane's row slot: new token i = r / G sees tokens below L - n + i + 1.
+  // This lane's row slot in tile t: new token i = r / G sees tokens below
+  // L - n + i + 1.
   const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;
   const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
-  const int r = r0 + (lane & 15);
-  const bool valid = r < rows;
-  Policy pol;
-  pol.init_rows(valid ? q + mq_out_row<G>(first, r, h, Hq) * D : nullptr, lane, row_bytes);
-  const int row_end = valid ? min(t_end, L - n_new + r / G + 1) : 0;
+  Policy pol[NT];
+  int row_end[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int r = r0 + t * kMqRows + (lane & 15);
+    const bool valid = r < rows;
+    pol[t].init_rows(valid ? q + mq_out_row<G>(first, r, h, Hq) * D : nullptr, lane, row_bytes);
+    row_end[t] = valid ? min(t_end, L - n_new + r / G + 1) : 0;
+  }
 
   const char* kbase = (const char*)(k_cache + (size_t)h * D);
   const char* vbase = (const char*)(v_cache + (size_t)h * D);
@@ -149,7 +156,7 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
       const int nrows = min(kBlockTokens, t_end - tok_of(k));
       const uint32_t extent = real ? (uint32_t)(nrows - 1) * row_bytes + D * 2u : 0u;
       const size_t o = (size_t)blk * block_bytes;
-      pol.load(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
+      pol[0].load(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
     };
 #pragma unroll
     for (int j = 0; j < NPF - 1; ++j) load_block(f[j], j);
@@ -158,40 +165,48 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
       for (int j = 0; j < NPF; ++j) {
         const int k = k0 + j;
         load_block(f[(j + NPF - 1) % NPF], k + NPF - 1);
-        pol.step(f[j], tok_of(k), row_end, sh.scale_log2);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pol[t].step(f[j], tok_of(k), row_end[t], sh.scale_log2);
         if (k + 1 >= my_blocks) goto blocks_done;
       }
     }
   blocks_done:;
   }
-  pol.to_lds(sm_m[wave], sm_l[wave], sm_o[wave]);
-  __syncthreads();
-
-  // Merge the waves in order; write each row, or its partial state.
+  // Merge the waves in order, one tile at a time through LDS; write each
+  // row, or its partial state.
   const int parts_of_seq = (L + P - 1) / P;
-  for (int idx = threadIdx.x; idx < nrow * D; idx += W * 64) {
-    const int rl = idx / D;
-    const int d = idx % D;
-    float mm = sm_m[0][rl];
 #pragma unroll
-    for (int w = 1; w < W; ++w) mm = fmaxf(mm, sm_m[w][rl]);
-    float lsum = 0.0f, o = 0.0f;
+  for (int t = 0; t < NT; ++t) {
+    const int tr0 = r0 + t * kMqRows;
+    const int tnrow = min(kMqRows, rows - tr0);   // uniform: rows of this tile in use
+    if (tnrow <= 0) break;
+    if (t > 0) __syncthreads();                   // the previous tile's LDS has been read
+    pol[t].to_lds(sm_m[wave], sm_l[wave], sm_o[wave]);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < tnrow * D; idx += W * 64) {
+      const int rl = idx / D;
+      const int d = idx % D;
+      float mm = sm_m[0][rl];
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float fw = fast_exp2(sm_m[w][rl] - mm);
-      lsum = fmaf(sm_l[w][rl], fw, lsum);
-      o = fmaf(sm_o[w][rl * D + d], fw, o);
-    }
-    const float res = lsum > 0.0f ? o / lsum : 0.0f;
-    const size_t orow = mq_out_row<G>(first, r0 + rl, h, Hq);
-    if (parts_of_seq == 1) {
-      out[orow * D + d] = E::round(res);
-    } else {
-      const size_t slot = orow * sh.num_parts + part;
-      ws_o[slot * D + d] = res;
-      if (d == 0) {
-        ws_ml[slot * 2] = mm;
-        ws_ml[slot * 2 + 1] = lsum;
+      for (int w = 1; w < W; ++w) mm = fmaxf(mm, sm_m[w][rl]);
+      float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float fw = fast_exp2(sm_m[w][rl] - mm);
+        lsum = fmaf(sm_l[w][rl], fw, lsum);
+        o = fmaf(sm_o[w][rl * D + d], fw, o);
+      }
+      const float res = lsum > 0.0f ? o / lsum : 0.0f;
+      const size_t orow = mq_out_row<G>(first, tr0 + rl, h, Hq);
+      if (parts_of_seq == 1) {
+        out[orow * D + d] = E::round(res);
+      } else {
+        const size_t slot = orow * sh.num_parts + part;
+        ws_o[slot * D + d] = res;
+        if (d == 0) {
+          ws_ml[slot * 2] = mm;
+          ws_ml[slot * 2 + 1] = lsum;
+        }
       }
     }
   }
@@ -201,7 +216,7 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
 // several partitions: out = sum_p w_p o_p / sum_p w_p with
 // w_p = l_p 2^(m_p - max m), over the partitions in index order. A partition
 // that holds none of a row's visible tokens has l_p = 0 and weighs nothing.
-template <int DT, int D, int G>
+template <int DT, int D, int G, int NT>
 __global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
@@ -216,18 +231,21 @@ __global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
   const int first = query_start[s];
   const int n_new = min(max(query_start[s + 1] - first, 0), sh.max_query_len);
   const int rows = n_new * G;
-  const int r0 = it.rg * kMqRows;
+  const int r0 = it.rg * (NT * kMqRows);
   if (r0 >= rows) return;
-  const int nrow = min(kMqRows, rows - r0);
+  const int nrow = min(NT * kMqRows, rows - r0);
   const int Hq = sh.num_kv_heads * G;
   for (int idx = threadIdx.x; idx < nrow * D; idx += kMqMergeThreads) {
     const int d = idx % D;
     const size_t orow = mq_out_row<G>(first, r0 + idx / D, h, Hq);
     const float* ml = ws_ml + orow * sh.num_parts * 2;
     const float* o = ws_o + orow * sh.num_parts * D + d;
+    // unrolled so that a chunk's loads are in flight together
     float mm = -INFINITY;
+#pragma unroll 8
     for (int p = 0; p < parts; ++p) mm = fmaxf(mm, ml[2 * p]);
     float acc = 0.0f, tot = 0.0f;
+#pragma unroll 8
     for (int p = 0; p < parts; ++p) {
       const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - mm);
       acc = fmaf(w, o[(size_t)p * D], acc);
@@ -237,13 +255,13 @@ __global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
   }
 }
 
-template <int DT, int D, int G, int W>
+template <int DT, int D, int G, int W, int NT>
 hipError_t launch_mq_typed(const MultiQueryArgs& a, hipStream_t stream) {
   MqShape sh{a.num_seqs,       a.num_kv_heads, a.num_blocks,       a.max_blocks_per_seq,
              a.max_context_len, a.max_query_len, a.partition_tokens, a.num_parts,
              a.row_groups,      a.scale_log2};
   const int64_t items = (int64_t)a.row_groups * a.num_seqs * a.num_kv_heads * a.num_parts;
-  hipLaunchKernelGGL((paged_mq_partition_kernel<DT, D, G, W>), dim3((unsigned)items),
+  hipLaunchKernelGGL((paged_mq_partition_kernel<DT, D, G, W, NT>), dim3((unsigned)items),
                      dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                      (const uint16_t*)a.v_cache, a.block_tables, a.context_lens, a.query_start,
@@ -251,17 +269,29 @@ hipError_t launch_mq_typed(const MultiQueryArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_parts <= 1) return err;
   const int64_t groups = (int64_t)a.row_groups * a.num_seqs * a.num_kv_heads;
-  hipLaunchKernelGGL((paged_mq_merge_kernel<DT, D, G>), dim3((unsigned)groups),
+  hipLaunchKernelGGL((paged_mq_merge_kernel<DT, D, G, NT>), dim3((unsigned)groups),
                      dim3(kMqMergeThreads), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
                      a.context_lens, a.query_start, sh);
   return hipGetLastError();
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, int NT>
 hipError_t launch_mq_waves(const MultiQueryArgs& a, hipStream_t stream) {
   switch (a.waves) {
-    case 4: return launch_mq_typed<DT, D, G, 4>(a, stream);
-    case 8: return launch_mq_typed<DT, D, G, 8>(a, stream);
+    case 4: return launch_mq_typed<DT, D, G, 4, NT>(a, stream);
+    case 8: return launch_mq_typed<DT, D, G, 8, NT>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT, int D, int G>
+hipError_t launch_mq_tiles(const MultiQueryArgs& a, hipStream_t stream) {
+  switch (a.tiles) {
+    case 1: return launch_mq_waves<DT, D, G, 1>(a, stream);
+    case 2: return launch_mq_waves<DT, D, G, 2>(a, stream);
+    case 4:
+      if constexpr (D == 64) return launch_mq_waves<DT, D, G, 4>(a, stream);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -269,10 +299,10 @@ hipError_t launch_mq_waves(const MultiQueryArgs& a, hipStream_t stream) {
 template <int DT, int D>
 hipError_t launch_mq_group(const MultiQueryArgs& a, int group, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_mq_waves<DT, D, 1>(a, stream);
-    case 2: return launch_mq_waves<DT, D, 2>(a, stream);
-    case 4: return launch_mq_waves<DT, D, 4>(a, stream);
-    case 8: return launch_mq_waves<DT, D, 8>(a, stream);
+    case 1: return launch_mq_tiles<DT, D, 1>(a, stream);
+    case 2: return launch_mq_tiles<DT, D, 2>(a, stream);
+    case 4: return launch_mq_tiles<DT, D, 4>(a, stream);
+    case 8: return launch_mq_tiles<DT, D, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
