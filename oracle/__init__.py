@@ -1,5 +1,5 @@
 """CPU float64 oracle for paged-attention decode (one or several new tokens per
-sequence) and the paged cache write.
+sequence), prefill attention and the paged cache write.
 
 TEST INFRASTRUCTURE ONLY: imported by `tests/`, `__graft_entry__.smoke()` and
 the `cpu_baseline` leg of `bench.py`, never by the product path. It shares no
@@ -16,6 +16,7 @@ from .paged_attention import (  # noqa: F401
     paged_decode,
     paged_decode_partitioned,
     paged_multi_query,
+    prefill_attention,
     round_to_storage,
     widen,
 )

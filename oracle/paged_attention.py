@@ -33,6 +33,11 @@ What is computed, and where it comes from:
   cached tokens (their K/V rows are in the pools), and new token i, at
   position L - n + i, attends causally over positions 0..L - n + i: exact
   softmax attention over that prefix, in float64.
+* Prefill: a new prompt's tokens attend causally among themselves, the step
+  before decode (mini-vllm write-up, section "1. 连续批处理": the scheduler
+  mixes prefill of new requests with decode of running ones; "关键工程决策"
+  item 2: one forward pass per admitted request). Token t of a prompt attends
+  over its tokens 0..t, reading the prompt's own K/V rows.
 * Cache write: new token i's K/V row goes to flat slot `slot_mapping[i]`,
   i.e. block `slot // block_size`, offset `slot % block_size`; negative slots
   are padding and are skipped. This is a raw copy, so it is bit-exact.
@@ -56,6 +61,7 @@ __all__ = [
     "paged_decode",
     "paged_decode_partitioned",
     "paged_multi_query",
+    "prefill_attention",
     "round_to_storage",
 ]
 
@@ -274,3 +280,35 @@ def paged_multi_query(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                 e = np.exp(z)
                 out[row, j] = (e / e.sum()) @ vs[:visible, h, :]
     return out
+
+
+def prefill_attention(q: np.ndarray, key: np.ndarray, value: np.ndarray,
+                      cu_seqlens: np.ndarray, scale: float, dtype: str) -> np.ndarray:
+    """Exact causal self-attention of new prompts, in float64.
+
+    q: `[T, Hq, D]`, key/value: `[T, Hkv, D]` raw bits, all prompts packed;
+    prompt s owns rows cu_seqlens[s] .. cu_seqlens[s+1]-1. Token t of a
+    prompt (row cu_seqlens[s] + t) attends over the prompt's rows 0..t, query
+    head j reading KV head j // (Hq / Hkv). Returns float64 `[T, Hq, D]`.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, Hq, D = q.shape
+    if key.shape != value.shape or key.shape[0] != T or key.shape[2] != D or Hq % key.shape[1]:
+        raise ValueError("q / key / value shapes do not match")
+    if cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must run from 0 to T without decreasing")
+    group = Hq // key.shape[1]
+    qf, kf, vf = widen(q, dtype), widen(key, dtype), widen(value, dtype)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        for t in range(hi - lo):
+            row = lo + t
+            for j in range(Hq):
+                h = j // group
+                z = scale * (kf[lo:row + 1, h, :] @ qf[row, j])
+                z = z - z.max()
+                e = np.exp(z)
+                out[row, j] = (e / e.sum()) @ vf[lo:row + 1, h, :]
+    return out
+

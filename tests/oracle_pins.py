@@ -439,4 +439,70 @@ def pin_mq_permutation_invariance(o):
     assert np.array_equal(got, ref)
 
 
+# ---------------------------------------------------------------- prefill
+
+def prefill_case(rng, dtype, lens, hq, hkv, d):
+    q = random_dyadic(rng, (sum(lens), hq, d))
+    k = random_dyadic(rng, (sum(lens), hkv, d))
+    v = random_dyadic(rng, (sum(lens), hkv, d))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return dict(qf=q, kf=k, vf=v, q=bits_of(q, dtype), k=bits_of(k, dtype), v=bits_of(v, dtype),
+                cu=cu, lens=list(lens), dtype=dtype)
+
+
+def run_prefill(o, c, scale):
+    return o.prefill_attention(c["q"], c["k"], c["v"], c["cu"], scale, c["dtype"])
+
+
+def pin_prefill_torch_sdpa_causal(o):
+    import torch
+    rng = np.random.default_rng(30)
+    c = prefill_case(rng, "bf16", [9, 1, 24], 8, 2, 16)
+    got = run_prefill(o, c, 0.3)
+    for s, n in enumerate(c["lens"]):
+        lo = int(c["cu"][s])
+        q = torch.tensor(c["qf"][lo:lo + n]).permute(1, 0, 2)                        # [Hq, n, D]
+        k = torch.tensor(np.repeat(c["kf"][lo:lo + n], 4, axis=1)).permute(1, 0, 2)
+        v = torch.tensor(np.repeat(c["vf"][lo:lo + n], 4, axis=1)).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=0.3)
+        assert np.allclose(got[lo:lo + n], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12), s
+
+
+def pin_prefill_bruteforce(o):
+    rng = np.random.default_rng(31)
+    c = prefill_case(rng, "f16", [5, 17, 2], 4, 2, 8)
+    got = run_prefill(o, c, 0.6)
+    for s, n in enumerate(c["lens"]):
+        lo = int(c["cu"][s])
+        for t in range(n):
+            ref = attend_contiguous(c["qf"][lo + t].tolist(), c["kf"][lo:lo + t + 1].tolist(),
+                                    c["vf"][lo:lo + t + 1].tolist(), 0.6, 2)
+            assert np.allclose(got[lo + t], np.array(ref), rtol=0, atol=1e-12), (s, t)
+
+
+def pin_prefill_first_token_returns_v0(o):
+    rng = np.random.default_rng(32)
+    c = prefill_case(rng, "bf16", [3, 7], 4, 2, 8)
+    got = run_prefill(o, c, 5.0)
+    for s in range(2):
+        lo = int(c["cu"][s])
+        for j in range(4):
+            assert np.array_equal(got[lo, j], c["vf"][lo, j // 2]), (s, j)
+
+
+def pin_prefill_equals_multi_query_all_new(o):
+    """A prompt whose rows sit in a paged cache is the multi-query case with
+    every token new (n = L): the two definitions must agree."""
+    rng = np.random.default_rng(33)
+    lens = [12, 33, 1]
+    c = prefill_case(rng, "f16", lens, 8, 2, 8)
+    got = run_prefill(o, c, 0.45)
+    k_seq = [c["kf"][c["cu"][s]:c["cu"][s + 1]] for s in range(3)]
+    v_seq = [c["vf"][c["cu"][s]:c["cu"][s + 1]] for s in range(3)]
+    kp, vp, tb = build_paged(np.random.default_rng(330), k_seq, v_seq, 8, "f16")
+    ref = o.paged_multi_query(c["q"], kp, vp, tb, np.array(lens, dtype=np.int32), c["cu"], 0.45,
+                              "f16")
+    assert np.allclose(got, ref, rtol=0, atol=1e-13)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

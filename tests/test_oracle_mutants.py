@@ -29,6 +29,10 @@ MUTANTS = {
     "mq_causal_off_by_one": ("visible = length - n_new + i + 1", "visible = length - n_new + i + 2"),
     "mq_positions_from_start": ("visible = length - n_new + i + 1", "visible = i + 1"),
     "mq_query_rows_reversed": ("row = first + i\n", "row = first + n_new - 1 - i\n"),
+    "prefill_not_causal": ("row + 1", "hi"),
+    "prefill_crosses_prompts": ("lo:row + 1", "0:row + 1"),
+    "prefill_head_mapping": ("                h = j // group\n                z = scale * (kf",
+                             "                h = j % key.shape[1]\n                z = scale * (kf"),
     "length_ignores_last_token": ("length = int(context_lens[s])\n        if length <= 0:\n            weights",
                                   "length = int(context_lens[s]) - 1\n        if length <= 0:\n            weights"),
 }
