@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MVK_ABI_VERSION 3
+#define MVK_ABI_VERSION 4
 
 typedef enum mvk_status {
     MVK_OK = 0,
@@ -256,6 +256,41 @@ int32_t mvk_paged_attention_multi_query(void* out, const void* q,
                                         int32_t max_blocks_per_seq, int32_t max_context_len,
                                         float scale, int32_t dtype, int32_t partition_tokens,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mvk_prefill_attention - causal self-attention of new prompts, with their
+ * K/V rows stored into the paged pools in the same call: the pass a request
+ * runs over its whole prompt when it is admitted, before it decodes
+ * ("从零手写 vLLM 核心：mini-vllm 项目深度解析", section "1. 连续批处理" and
+ * "关键工程决策" item 2).
+ *
+ * Defines, for prompt s owning rows lo = cu_seqlens[s] .. cu_seqlens[s+1]-1,
+ * its token t (row lo + t), query head j and h = j / g:
+ *   out[lo+t][j] = sum_{u <= t} softmax_u(scale * q[lo+t][j] . key[lo+u][h]) value[lo+u][h]
+ * and, when slot_mapping is given, stores key[r] / value[r] at flat slot
+ * slot_mapping[r] of k_cache / v_cache exactly as mvk_reshape_and_cache would
+ * (negative slots skipped). Attention reads the key/value tensors, not the
+ * pools. Arithmetic and rounding as for mvk_paged_attention_decode.
+ *
+ *   out, q        [num_tokens, num_q_heads, head_dim], dtype; out written.
+ *   key, value    [num_tokens, num_kv_heads, head_dim], dtype.
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim], dtype;
+ *   v_cache       written at slot_mapping; ignored (may be NULL) without it.
+ *   slot_mapping  int32 [num_tokens] or NULL (no cache write).
+ *   cu_seqlens    int32 [num_seqs + 1], on the device: 0 = cu_seqlens[0] <=
+ *                 ... <= cu_seqlens[num_seqs] = num_tokens, every prompt
+ *                 length <= max_seqlen (host-side bound that sizes the grid).
+ *   head_dim 64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
+ *   block_size 16. num_seqs == 0 or num_tokens == 0 is a no-op.
+ * Repeated calls give identical bits.
+ * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED, MVK_ERR_HIP.
+ */
+int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const void* value,
+                              void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_tokens,
+                              int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              float scale, int32_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,8 @@ is no fallback: if libmvk.so is missing, the first call fails with instructions.
                                 query_start, scale, max_query_len=None,
                                 max_context_len=None, out=None, partition_tokens=0,
                                 workspace=None)
+    prefill_attention(q, key, value, cu_seqlens, scale, max_seqlen=None,
+                      k_cache=None, v_cache=None, slot_mapping=None, out=None)
 
 The loader relies on torch having loaded its HIP runtime first: the library's
 dependency on libamdhip64.so.7 then resolves to that same runtime, so the
@@ -28,7 +30,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmvk.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MVK_OK = 0
 MVK_ERR_INVALID_ARGUMENT = 1
 MVK_ERR_UNSUPPORTED = 2
@@ -56,6 +58,9 @@ SIGNATURES = {
     "mvk_paged_attention_multi_query_workspace_size": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                  ctypes.POINTER(_c_size), ctypes.POINTER(_c_int)]),
+    "mvk_prefill_attention": (
+        _c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int,
+                 _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _ptr]),
     "mvk_paged_attention_multi_query": (
         _c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _ptr, _c_size,
@@ -301,5 +306,54 @@ def paged_attention_multi_query(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
         max_query_len, hq, hkv, d, bs, nb, block_tables.shape[1], max_context_len, float(scale),
         _dtype_code(q), partition_tokens, ws_ptr, ws_bytes, _stream(q.device))
     _check("mvk_paged_attention_multi_query", st)
+    return out
+
+
+def prefill_attention(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                      cu_seqlens: torch.Tensor, scale: float, max_seqlen: int | None = None,
+                      k_cache: torch.Tensor | None = None, v_cache: torch.Tensor | None = None,
+                      slot_mapping: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal self-attention of packed new prompts (prompt s owns rows
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 of q [T, Hq, D] and key/value
+    [T, Hkv, D]); with k_cache / v_cache / slot_mapping the rows of key/value
+    are also stored into the pools at their slots. `max_seqlen` bounds the
+    prompt lengths; when omitted it is read from the device (a synchronising
+    copy)."""
+    _require(q, "q", ndim=3)
+    _require(key, "key", dtype=q.dtype, ndim=3)
+    _require(value, "value", dtype=q.dtype, ndim=3)
+    _require(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1)
+    T, hq, d = q.shape
+    S = cu_seqlens.shape[0] - 1
+    if key.shape != value.shape or key.shape[0] != T or key.shape[2] != d or S < 0:
+        raise ValueError("inconsistent shapes")
+    hkv = key.shape[1]
+    write = (k_cache, v_cache, slot_mapping)
+    if any(t is not None for t in write):
+        if any(t is None for t in write):
+            raise ValueError("k_cache, v_cache and slot_mapping go together")
+        _require(k_cache, "k_cache", dtype=q.dtype, ndim=4)
+        _require(v_cache, "v_cache", dtype=q.dtype, ndim=4)
+        _require(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+        nb, bs, hkv2, d2 = k_cache.shape
+        if v_cache.shape != k_cache.shape or (hkv2, d2) != (hkv, d) or slot_mapping.shape[0] != T:
+            raise ValueError("inconsistent cache shapes")
+        kc, vc, sm = k_cache.data_ptr(), v_cache.data_ptr(), slot_mapping.data_ptr()
+    else:
+        nb, bs, kc, vc, sm = 0, 16, None, None, None
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if S else 0
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", dtype=q.dtype)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    st = lib().mvk_prefill_attention(out.data_ptr(), q.data_ptr(), key.data_ptr(),
+                                     value.data_ptr(), kc, vc, sm, cu_seqlens.data_ptr(), S, T,
+                                     max_seqlen, hq, hkv, d, bs, nb, float(scale), _dtype_code(q),
+                                     _stream(q.device))
+    _check("mvk_prefill_attention", st)
     return out
 

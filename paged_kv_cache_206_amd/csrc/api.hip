@@ -390,4 +390,52 @@ int32_t mvk_paged_attention_multi_query(
   return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
 }
 
+int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const void* value,
+                              void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_tokens,
+                              int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              float scale, int32_t dtype, void* stream) {
+  if (dtype != MVK_F16 && dtype != MVK_BF16) return MVK_ERR_INVALID_ARGUMENT;
+  if (block_size != kBlock) return MVK_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_tokens < 0 || max_seqlen < 0 ||
+      num_q_heads <= 0 || num_q_heads > kMaxGridYZ || num_kv_heads <= 0 || !isfinite(scale))
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return MVK_ERR_INVALID_ARGUMENT;
+  if (!mvk::decode_supported(head_dim, num_q_heads / num_kv_heads)) return MVK_ERR_UNSUPPORTED;
+  if ((int64_t)num_tokens > (int64_t)num_seqs * max_seqlen) return MVK_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0 || num_tokens == 0) return MVK_OK;
+  if (!out || !q || !key || !value || !cu_seqlens) return MVK_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(key) || !aligned16(value) ||
+      !aligned4(cu_seqlens))
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (out == q || out == key || out == value) return MVK_ERR_INVALID_ARGUMENT;
+  if (slot_mapping) {  // the fused cache write
+    if (!k_cache || !v_cache || k_cache == v_cache || num_blocks <= 0) return MVK_ERR_INVALID_ARGUMENT;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned4(slot_mapping))
+      return MVK_ERR_INVALID_ARGUMENT;
+    if ((int64_t)num_blocks * kBlock > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
+    if (out == k_cache || out == v_cache) return MVK_ERR_INVALID_ARGUMENT;
+  }
+  mvk::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.key = key;
+  a.value = value;
+  a.k_cache = slot_mapping ? k_cache : nullptr;
+  a.v_cache = slot_mapping ? v_cache : nullptr;
+  a.slot_mapping = slot_mapping;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.max_seqlen = max_seqlen;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = slot_mapping ? num_blocks : 0;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  a.dtype = dtype;
+  hipError_t err = mvk::launch_prefill(a, (hipStream_t)stream);
+  return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
+}
+
 }  // extern "C"

@@ -116,6 +116,16 @@ struct MfmaPolicy {
     }
   }
 
+  // The same fragment from a tile in LDS: token rows row_bytes apart, the
+  // same pitch init_rows was given.
+  __device__ __forceinline__ void load_lds(Frag& f, const char* k_tile, const char* v_tile,
+                                           uint32_t row_bytes) const {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) f.k[ks] = *(const uint4*)(k_tile + koff + 64u * ks);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = *(const VT*)(v_tile + voff + i * row_bytes);
+  }
+
   // Decode: every row slot j < G sees the block's tokens below t_end.
   // nk/nv: the step's new K/V row of this KV head in LDS, as 16-byte chunks
   __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub,

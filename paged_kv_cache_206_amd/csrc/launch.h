@@ -64,4 +64,20 @@ struct MultiQueryArgs {
 
 hipError_t launch_paged_multi_query(const MultiQueryArgs& a, hipStream_t stream);
 
+struct PrefillArgs {
+  void* out;                    // [T, Hq, D]
+  const void* q;                // [T, Hq, D]
+  const void* key;              // [T, Hkv, D] the prompts' new K/V rows
+  const void* value;
+  void* k_cache;                // pools, written at slot_mapping (nullptr slot_mapping: no write)
+  void* v_cache;
+  const int32_t* slot_mapping;  // [T] or nullptr
+  const int32_t* cu_seqlens;    // [S + 1]: prompt s owns rows [cu_seqlens[s], cu_seqlens[s+1])
+  int32_t num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim, num_blocks;
+  float scale_log2;
+  int32_t dtype;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 }  // namespace mvk

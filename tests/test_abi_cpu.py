@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "mvk_abi_version", "mvk_status_string", "mvk_reshape_and_cache",
         "mvk_paged_attention_workspace_size", "mvk_paged_attention_decode",
-        "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query"])
+        "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query",
+        "mvk_prefill_attention"])
 
 
 def test_library_exports_every_declared_symbol(mvk):
@@ -48,7 +49,7 @@ def test_single_hip_runtime_mapped(mvk):
 
 
 def test_version_and_status_strings(mvk):
-    assert mvk.abi_version() == 3
+    assert mvk.abi_version() == 4
     assert mvk.status_string(0) == "ok"
     assert mvk.status_string(3) == "workspace too small"
     assert mvk.status_string(99) == "unknown status"
@@ -191,4 +192,40 @@ def test_multi_query_workspace_size(mvk):
     assert p == 512 and nbytes == 160 * 32 * 64 * (128 + 2) * 4
     with pytest.raises(mvk.MvkError):
         mvk.multi_query_workspace_size(2, 3, 0, 4, 2, 64, 10)
+
+
+def prefill_call(mvk, **over):
+    a = dict(out=FAKE, q=FAKE * 2, key=FAKE * 3, value=FAKE * 4, kc=FAKE * 5, vc=FAKE * 6,
+             sm=FAKE * 7, cu=FAKE * 8, S=2, T=40, maxlen=30, hq=8, hkv=2, d=128, bs=16, nb=8,
+             scale=0.1, dtype=1, stream=None)
+    a.update(over)
+    return mvk.lib().mvk_prefill_attention(
+        a["out"], a["q"], a["key"], a["value"], a["kc"], a["vc"], a["sm"], a["cu"], a["S"],
+        a["T"], a["maxlen"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=5), 1),
+    (dict(bs=8), 2),
+    (dict(d=80), 2),
+    (dict(hq=12, hkv=8), 1),
+    (dict(hq=32, hkv=2), 2),
+    (dict(T=61), 1),                  # more tokens than num_seqs * max_seqlen
+    (dict(S=-1), 1),
+    (dict(scale=math.inf), 1),
+    (dict(cu=None), 1),
+    (dict(key=FAKE * 3 + 8), 1),      # misaligned
+    (dict(out=FAKE * 3), 1),          # out aliases key
+    (dict(vc=FAKE * 5), 1),           # the fused write needs two distinct pools
+    (dict(kc=None), 1),
+    (dict(nb=0), 1),
+])
+def test_prefill_validation(mvk, over, status):
+    assert prefill_call(mvk, **over) == status
+
+
+def test_prefill_noop(mvk):
+    assert prefill_call(mvk, S=0, T=0, out=None, q=None) == 0
+    assert prefill_call(mvk, T=0, out=None, q=None) == 0
 

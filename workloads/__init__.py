@@ -204,6 +204,60 @@ def make_queries(wl: Workload, new_tokens, seed: int, device="cpu"):
     return q, query_start
 
 
+@dataclass
+class Prefill:
+    """New prompts packed along the token axis, plus a paged cache to store
+    their K/V rows in: prompt s owns rows cu_seqlens[s] .. cu_seqlens[s+1]-1,
+    and row r goes to flat slot slot_mapping[r] (through the prompt's own
+    blocks of block_tables)."""
+    dtype: str
+    q: torch.Tensor            # [T, Hq, D]
+    key: torch.Tensor          # [T, Hkv, D]
+    value: torch.Tensor        # [T, Hkv, D]
+    cu_seqlens: torch.Tensor   # int32 [S + 1]
+    k_cache: torch.Tensor      # [NB, 16, Hkv, D]
+    v_cache: torch.Tensor
+    block_tables: torch.Tensor  # int32 [S, max_blocks]
+    slot_mapping: torch.Tensor  # int32 [T]
+    scale: float
+
+    @property
+    def max_seqlen(self) -> int:
+        return int((self.cu_seqlens[1:] - self.cu_seqlens[:-1]).max().item()) \
+            if self.cu_seqlens.numel() > 1 else 0
+
+    def to(self, device) -> "Prefill":
+        return Prefill(self.dtype, *(t.to(device) for t in (
+            self.q, self.key, self.value, self.cu_seqlens, self.k_cache, self.v_cache,
+            self.block_tables, self.slot_mapping)), self.scale)
+
+
+def make_prefill(dtype, prompt_lens, num_q_heads, num_kv_heads, head_dim, seed,
+                 extra_blocks=4, device="cpu") -> Prefill:
+    """Seeded prompts: N(0, 1) q / key / value rows; each prompt gets random
+    distinct physical blocks of a pool filled with N(0, 1) values, and its
+    rows' slots follow its block table."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = torch.as_tensor(prompt_lens, dtype=torch.int32)
+    nb = int(((lens + BLOCK_SIZE - 1) // BLOCK_SIZE).sum()) + extra_blocks
+    tables, _ = assign_blocks(lens, nb, gen)
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    slots = []
+    for s, L in enumerate(lens.tolist()):
+        for t in range(L):
+            slots.append(int(tables[s, t // BLOCK_SIZE]) * BLOCK_SIZE + t % BLOCK_SIZE)
+    T = int(cu[-1])
+    vgen = _value_gen(seed, device)
+    q = randn_storage((T, num_q_heads, head_dim), dtype, vgen, device)
+    key = randn_storage((T, num_kv_heads, head_dim), dtype, vgen, device)
+    value = randn_storage((T, num_kv_heads, head_dim), dtype, vgen, device)
+    k_cache = randn_storage((nb, BLOCK_SIZE, num_kv_heads, head_dim), dtype, vgen, device)
+    v_cache = randn_storage((nb, BLOCK_SIZE, num_kv_heads, head_dim), dtype, vgen, device)
+    return Prefill(dtype, q, key, value, cu, k_cache, v_cache, tables,
+                   torch.tensor(slots, dtype=torch.int32), 1.0 / math.sqrt(head_dim))
+
+
 def make_custom(name, dtype, context_lens, num_q_heads, num_kv_heads, head_dim, num_blocks,
                 seed, layers=1, shared_prefix=None, new_rows=True, scale=None,
                 value_device="cpu", values=True) -> Workload:
