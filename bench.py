@@ -26,6 +26,12 @@ With --new-tokens N > 1 the step is instead, for every layer, one
 multi-query call in which each sequence brings N new tokens (the last
 accepted token and N - 1 draft tokens of speculative decoding), causal among
 them; the roofline then covers that kernel.
+
+With --prefill LEN the step is one prefill call per layer over the
+workload's sequences as new prompts of LEN tokens each (causal
+self-attention, their K/V rows written into the pools in the same call); it
+is compute-bound, so its roofline is against the dense MFMA peak of the
+storage type.
 """
 from __future__ import annotations
 
@@ -36,6 +42,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16 / bf16 matrix peak
 
 WORKLOAD_TEXT = {
     "qwen3": "Qwen3-0.6B-shaped decode step: 60 seqs, context U[64,256], 16 q / 8 kv heads, "
@@ -64,6 +71,8 @@ def parse_args():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, --steps times (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
+    ap.add_argument("--prefill", type=int, default=0, metavar="LEN",
+                    help="prefill prompts of LEN tokens instead of decode")
     ap.add_argument("--new-tokens", type=int, default=1, metavar="N",
                     help="new tokens per sequence; N > 1 runs the multi-query kernel")
     ap.add_argument("--unfused", action="store_true",
@@ -102,6 +111,9 @@ def main():
     slots = wl.slot_mapping.to(dev)
     S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     maxlen = wl.max_context_len
+    if args.prefill > 0:
+        run_prefill(args, torch, mvk, W, wl, nlayers_step, dev)
+        return
     if args.new_tokens > 1:
         run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt, cl, dev)
         return
@@ -363,6 +375,70 @@ def run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt
     if not args.no_cpu and args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline_multi_query(wl, layers[:nlayers_step], queries, qs,
                                                           args.cpu_seconds, kv_logical)
+    print(json.dumps(result), flush=True)
+
+
+def run_prefill(args, torch, mvk, W, wl, nlayers_step, dev):
+    """The step as prefill: every sequence of the workload arrives as a new
+    prompt of args.prefill tokens; one prefill call per layer (fused cache
+    write), timed in a graph of back-to-back calls over rotating inputs."""
+    S, Hq, Hkv, D, L = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, args.prefill
+    nsets = max(1, min(nlayers_step, 4))
+    pfs = [W.make_prefill(wl.dtype, [L] * S, Hq, Hkv, D, seed=2000 + i, device="cuda").to(dev)
+           for i in range(nsets)]
+
+    def call(i):
+        p = pfs[i]
+        mvk.prefill_attention(p.q, p.key, p.value, p.cu_seqlens, p.scale, max_seqlen=L,
+                              k_cache=p.k_cache, v_cache=p.v_cache, slot_mapping=p.slot_mapping)
+
+    for _ in range(max(1, args.warmup)):
+        for i in range(nsets):
+            call(i)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // nsets)
+    per_call_us = graph_time_per_call(torch, dev, [lambda i=i: call(i) for i in range(nsets)], reps)
+    # causal: token t of a prompt meets t + 1 keys; 2 flop per multiply-add, QK and PV
+    flops = 4 * D * Hq * S * (L * (L + 1) // 2)
+    tflops = flops / (per_call_us * 1e-6) / 1e12
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    T = S * L
+    step_s = per_call_us * nlayers_step / 1e6
+    result = {
+        "metric": "paged-decode KV read GB/s (% of MI355X HBM peak); decode tokens/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": reps * nsets,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "launch": "hipgraph replay of back-to-back prefill calls",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/key/value rows, random block tables)",
+        "config": {
+            "workload": f"prefill of {S} prompts x {L} tokens, heads and dtype of: "
+                        + WORKLOAD_TEXT[args.workload],
+            "num_seqs": S, "prompt_len": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_dim": D, "block_size": 16, "layers_per_step": nlayers_step,
+            "cache_write": "fused into prefill", "input_sets": nsets,
+        },
+        "prompt_tokens_per_s": round(T / (per_call_us * 1e-6), 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_kernel (fused cache write)",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": None,
+            "alg_flops_per_launch": flops,
+            "launch_us": round(per_call_us, 3),
+            "launch_us_method": "hipgraph of back-to-back prefill calls, events around the replays",
+        },
+    }
     print(json.dumps(result), flush=True)
 
 
