@@ -50,14 +50,15 @@
 extern "C" {
 #endif
 
-#define MVK_ABI_VERSION 4
+#define MVK_ABI_VERSION 5
 
 typedef enum mvk_status {
     MVK_OK = 0,
     MVK_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misaligned tensor */
     MVK_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, group size, block size */
     MVK_ERR_WORKSPACE_TOO_SMALL = 3,
-    MVK_ERR_HIP = 4                 /* a HIP launch reported an error */
+    MVK_ERR_HIP = 4,                /* a HIP launch reported an error */
+    MVK_ERR_OUT_OF_BLOCKS = 5       /* block manager: not enough free KV blocks */
 } mvk_status;
 
 typedef enum mvk_dtype {
@@ -291,6 +292,82 @@ int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const v
                               int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
                               float scale, int32_t dtype, void* stream);
+
+/*
+ * Block manager (host side): which physical 16-token blocks each sequence
+ * owns, the block tables and slot mappings the calls above read, prefix
+ * sharing of full blocks, and release, eviction and rollback. The KV-cache
+ * manager owns logical blocks, block tables, the prefix cache, and block
+ * allocation and release (micro-vLLM wiki, layer description
+ * "KVCacheManager", feature list "Paged KV Cache、prefix cache 和请求抢占");
+ * blocks are allocated on demand, shared through prefix caching, and
+ * admission stays correct when blocks are scarce ("从零手写 vLLM 核心：
+ * mini-vllm 项目深度解析", section "2. 分页KV缓存（PagedAttention）");
+ * speculative decoding needs KV rollback (same write-up, "工程启示").
+ *
+ * Rules:
+ *  - A slot is a flat pool row: block * 16 + offset; token t of a sequence is
+ *    in table[t / 16] at offset t % 16.
+ *  - A full block is identified by the chained hash of its parent block and
+ *    its 16 token ids (checked against the ids on a hit). A new sequence
+ *    shares the cached blocks of its longest cached full-block prefix; the
+ *    block holding its last prompt token is always its own. Shared blocks are
+ *    reference counted.
+ *  - A released block goes to the back of the free queue; a block with a hash
+ *    stays findable until the queue hands it out again (least recently
+ *    released first). A sequence's blocks are released newest first, so its
+ *    prefix stays cached longest.
+ *  - Rollback drops a sequence's newest tokens and never modifies a block
+ *    another sequence shares (MVK_ERR_INVALID_ARGUMENT instead).
+ * Host memory only; not thread-safe (one manager per scheduler thread).
+ * Errors: MVK_ERR_INVALID_ARGUMENT (NULL manager or output, unknown or
+ * duplicate seq_id, bad sizes), MVK_ERR_OUT_OF_BLOCKS (nothing was changed).
+ */
+typedef struct mvk_block_manager mvk_block_manager;
+
+/* A manager of num_blocks blocks of block_size (16) tokens, all free; prefix
+ * sharing on when prefix_cache != 0. NULL on bad sizes or no memory. */
+mvk_block_manager* mvk_bm_create(int32_t num_blocks, int32_t block_size, int32_t prefix_cache);
+void mvk_bm_destroy(mvk_block_manager* m);
+
+/* Blocks in the free queue (cached ones included); -1 for a NULL manager. */
+int32_t mvk_bm_num_free(const mvk_block_manager* m);
+
+/* Whether a prompt of num_tokens token ids could be admitted now: MVK_OK or
+ * MVK_ERR_OUT_OF_BLOCKS; *cached_tokens (may be NULL) receives how many of its
+ * leading tokens are already cached. Changes nothing. */
+int32_t mvk_bm_can_admit(const mvk_block_manager* m, const int32_t* token_ids,
+                         int32_t num_tokens, int32_t* cached_tokens);
+
+/* Admit a prompt as sequence seq_id: share its cached prefix blocks, allocate
+ * the rest. *cached_tokens (may be NULL) receives the shared prefix length in
+ * tokens (its K/V rows need not be recomputed). */
+int32_t mvk_bm_admit(mvk_block_manager* m, int64_t seq_id, const int32_t* token_ids,
+                     int32_t num_tokens, int32_t* cached_tokens);
+
+/* Append one token (a decode step or a draft token); *slot receives its slot. */
+int32_t mvk_bm_append(mvk_block_manager* m, int64_t seq_id, int32_t token_id, int32_t* slot);
+
+/* Drop the sequence's newest num_tokens tokens (rejected drafts). */
+int32_t mvk_bm_rollback(mvk_block_manager* m, int64_t seq_id, int32_t num_tokens);
+
+/* Release a finished or preempted sequence. */
+int32_t mvk_bm_release(mvk_block_manager* m, int64_t seq_id);
+
+/* Tokens and blocks the sequence holds (either pointer may be NULL). */
+int32_t mvk_bm_seq_info(const mvk_block_manager* m, int64_t seq_id, int32_t* num_tokens,
+                        int32_t* num_blocks);
+
+/* The sequence's block table into table[0 .. max_blocks), -1 past its blocks. */
+int32_t mvk_bm_block_table(const mvk_block_manager* m, int64_t seq_id, int32_t* table,
+                           int32_t max_blocks);
+
+/* Slots of the sequence's tokens first_token .. first_token + count - 1. */
+int32_t mvk_bm_slots(const mvk_block_manager* m, int64_t seq_id, int32_t first_token,
+                     int32_t count, int32_t* slots);
+
+/* Reference count of a block (0 = free); -1 for a bad manager or block. */
+int32_t mvk_bm_block_ref(const mvk_block_manager* m, int32_t block);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@ is no fallback: if libmvk.so is missing, the first call fails with instructions.
                                 workspace=None)
     prefill_attention(q, key, value, cu_seqlens, scale, max_seqlen=None,
                       k_cache=None, v_cache=None, slot_mapping=None, out=None)
+    BlockManager(num_blocks, prefix_cache=True)   # host-side block tables and slots
 
 The loader relies on torch having loaded its HIP runtime first: the library's
 dependency on libamdhip64.so.7 then resolves to that same runtime, so the
@@ -30,12 +31,13 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmvk.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MVK_OK = 0
 MVK_ERR_INVALID_ARGUMENT = 1
 MVK_ERR_UNSUPPORTED = 2
 MVK_ERR_WORKSPACE_TOO_SMALL = 3
 MVK_ERR_HIP = 4
+MVK_ERR_OUT_OF_BLOCKS = 5
 MVK_F16 = 0
 MVK_BF16 = 1
 
@@ -65,6 +67,19 @@ SIGNATURES = {
         _c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _ptr, _c_size,
                  _ptr]),
+    "mvk_bm_create": (_ptr, [_c_int, _c_int, _c_int]),
+    "mvk_bm_destroy": (None, [_ptr]),
+    "mvk_bm_num_free": (_c_int, [_ptr]),
+    "mvk_bm_can_admit": (_c_int, [_ptr, _ptr, _c_int, ctypes.POINTER(_c_int)]),
+    "mvk_bm_admit": (_c_int, [_ptr, ctypes.c_int64, _ptr, _c_int, ctypes.POINTER(_c_int)]),
+    "mvk_bm_append": (_c_int, [_ptr, ctypes.c_int64, _c_int, ctypes.POINTER(_c_int)]),
+    "mvk_bm_rollback": (_c_int, [_ptr, ctypes.c_int64, _c_int]),
+    "mvk_bm_release": (_c_int, [_ptr, ctypes.c_int64]),
+    "mvk_bm_seq_info": (_c_int, [_ptr, ctypes.c_int64, ctypes.POINTER(_c_int),
+                                 ctypes.POINTER(_c_int)]),
+    "mvk_bm_block_table": (_c_int, [_ptr, ctypes.c_int64, _ptr, _c_int]),
+    "mvk_bm_slots": (_c_int, [_ptr, ctypes.c_int64, _c_int, _c_int, _ptr]),
+    "mvk_bm_block_ref": (_c_int, [_ptr, _c_int]),
 }
 
 
@@ -357,3 +372,88 @@ def prefill_attention(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
     _check("mvk_prefill_attention", st)
     return out
 
+
+
+def _int32_array(values) -> ctypes.Array:
+    vals = [int(v) for v in values]
+    return (ctypes.c_int32 * max(len(vals), 1))(*vals)
+
+
+class BlockManager:
+    """Host-side owner of the KV pools' 16-token blocks (libmvk's block manager):
+    per-sequence block tables and slot mappings, prefix sharing of full blocks,
+    release with least-recently-released reuse, and rollback of rejected draft
+    tokens. Out of blocks raises MvkError with status MVK_ERR_OUT_OF_BLOCKS and
+    changes nothing."""
+
+    BLOCK = 16
+
+    def __init__(self, num_blocks: int, prefix_cache: bool = True):
+        self._lib = lib()
+        self._h = self._lib.mvk_bm_create(num_blocks, self.BLOCK, 1 if prefix_cache else 0)
+        if not self._h:
+            raise ValueError(f"cannot create a block manager of {num_blocks} blocks")
+        self.num_blocks = num_blocks
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.mvk_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def num_free(self) -> int:
+        return self._lib.mvk_bm_num_free(self._h)
+
+    def can_admit(self, token_ids) -> tuple[bool, int]:
+        """(whether the prompt fits now, how many of its leading tokens are cached)."""
+        ids = _int32_array(token_ids)
+        cached = ctypes.c_int32(0)
+        st = self._lib.mvk_bm_can_admit(self._h, ids, len(token_ids), ctypes.byref(cached))
+        if st not in (MVK_OK, MVK_ERR_OUT_OF_BLOCKS):
+            raise MvkError("mvk_bm_can_admit", st)
+        return st == MVK_OK, cached.value
+
+    def admit(self, seq_id: int, token_ids) -> int:
+        """Admit a prompt; returns the number of leading tokens already cached."""
+        ids = _int32_array(token_ids)
+        cached = ctypes.c_int32(0)
+        _check("mvk_bm_admit", self._lib.mvk_bm_admit(self._h, seq_id, ids, len(token_ids),
+                                                      ctypes.byref(cached)))
+        return cached.value
+
+    def append(self, seq_id: int, token_id: int) -> int:
+        """Append one token; returns its slot."""
+        slot = ctypes.c_int32(0)
+        _check("mvk_bm_append", self._lib.mvk_bm_append(self._h, seq_id, token_id,
+                                                        ctypes.byref(slot)))
+        return slot.value
+
+    def rollback(self, seq_id: int, num_tokens: int) -> None:
+        _check("mvk_bm_rollback", self._lib.mvk_bm_rollback(self._h, seq_id, num_tokens))
+
+    def release(self, seq_id: int) -> None:
+        _check("mvk_bm_release", self._lib.mvk_bm_release(self._h, seq_id))
+
+    def seq_info(self, seq_id: int) -> tuple[int, int]:
+        """(tokens, blocks) the sequence holds."""
+        n, b = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check("mvk_bm_seq_info", self._lib.mvk_bm_seq_info(self._h, seq_id, ctypes.byref(n),
+                                                            ctypes.byref(b)))
+        return n.value, b.value
+
+    def block_table(self, seq_id: int, max_blocks: int) -> list[int]:
+        table = (ctypes.c_int32 * max(max_blocks, 1))()
+        _check("mvk_bm_block_table",
+               self._lib.mvk_bm_block_table(self._h, seq_id, table, max_blocks))
+        return list(table[:max_blocks])
+
+    def slots(self, seq_id: int, first_token: int, count: int) -> list[int]:
+        out = (ctypes.c_int32 * max(count, 1))()
+        _check("mvk_bm_slots", self._lib.mvk_bm_slots(self._h, seq_id, first_token, count, out))
+        return list(out[:count])
+
+    def block_ref(self, block: int) -> int:
+        return self._lib.mvk_bm_block_ref(self._h, block)

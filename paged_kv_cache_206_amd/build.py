@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_206_amd.build          # or build() from Python
 
-Every .hip file under csrc/ is compiled with hipcc for gfx950 only and linked
-into paged_kv_cache_206_amd/libmvk.so. Packed-fp32 instructions are disabled
+Every .hip file under csrc/ is compiled with hipcc for gfx950 only, every
+.cpp file (host-only code) with g++, and all are linked into
+paged_kv_cache_206_amd/libmvk.so. Packed-fp32 instructions are disabled
 (-packed-fp32-ops) for all device code.
 """
 from __future__ import annotations
@@ -42,6 +43,7 @@ def build(verbose: bool = False, defines=()) -> str:
     MVK_TUNE_P / MVK_TUNE_W environment variables, for tuning sweeps)."""
     cc = hipcc()
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    host_sources = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))  # host-only C++
     if not sources:
         raise RuntimeError(f"no HIP sources under {CSRC}")
     with tempfile.TemporaryDirectory(prefix="mvk_build_") as tmp:
@@ -50,6 +52,15 @@ def build(verbose: bool = False, defines=()) -> str:
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             cmd = [cc, *COMMON_FLAGS, *("-D" + d for d in defines), "-I", os.path.join(ROOT, "include"),
                    "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+            objs.append(obj)
+        for src in host_sources:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            cmd = [shutil.which("g++") or "g++", "-O2", "-std=c++17", "-fPIC", "-Wall",
+                   *("-D" + d for d in defines), "-I", os.path.join(ROOT, "include"), "-c", src,
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)

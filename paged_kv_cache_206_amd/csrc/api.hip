@@ -201,6 +201,7 @@ const char* mvk_status_string(int32_t status) {
     case MVK_ERR_UNSUPPORTED: return "unsupported configuration";
     case MVK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MVK_ERR_HIP: return "HIP error";
+    case MVK_ERR_OUT_OF_BLOCKS: return "not enough free KV blocks";
     default: return "unknown status";
   }
 }

@@ -32,7 +32,10 @@ def test_header_declares_the_boundary():
         "mvk_abi_version", "mvk_status_string", "mvk_reshape_and_cache",
         "mvk_paged_attention_workspace_size", "mvk_paged_attention_decode",
         "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query",
-        "mvk_prefill_attention"])
+        "mvk_prefill_attention",
+        "mvk_bm_create", "mvk_bm_destroy", "mvk_bm_num_free", "mvk_bm_can_admit", "mvk_bm_admit",
+        "mvk_bm_append", "mvk_bm_rollback", "mvk_bm_release", "mvk_bm_seq_info",
+        "mvk_bm_block_table", "mvk_bm_slots", "mvk_bm_block_ref"])
 
 
 def test_library_exports_every_declared_symbol(mvk):
@@ -49,9 +52,10 @@ def test_single_hip_runtime_mapped(mvk):
 
 
 def test_version_and_status_strings(mvk):
-    assert mvk.abi_version() == 4
+    assert mvk.abi_version() == 5
     assert mvk.status_string(0) == "ok"
     assert mvk.status_string(3) == "workspace too small"
+    assert mvk.status_string(5) == "not enough free KV blocks"
     assert mvk.status_string(99) == "unknown status"
 
 
