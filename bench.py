@@ -479,16 +479,32 @@ def cpu_baseline_multi_query(wl, layers, queries, qs, budget_s, kv_logical_per_l
     }
 
 
-def kernel_source_digest():
-    """sha256 over the library's kernel sources: traffic counters recorded for
-    other sources are stale."""
-    import glob
+KERNEL_SOURCES = {"paged_decode": "paged_decode.hip",
+                  "paged_multi_query": "paged_multi_query.hip",
+                  "prefill": "prefill.hip"}
+
+
+def kernel_source_digest(kind="paged_decode"):
+    """sha256 over the sources a kernel family is built from: its .hip file,
+    the local headers it includes (transitively), and api.hip (launch
+    planning). Traffic counters recorded for other sources are stale."""
     import hashlib
+    import re
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_206_amd",
+                        "csrc")
+    base = kind.split("_n")[0] if kind.startswith("paged_multi_query") else kind
+    todo, seen = [KERNEL_SOURCES[base], "api.hip"], set()
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.exists(os.path.join(csrc, name)):
+            continue
+        seen.add(name)
+        with open(os.path.join(csrc, name)) as f:
+            todo += re.findall(r'^#include "([^"]+)"', f.read(), flags=re.M)
     h = hashlib.sha256()
-    here = os.path.dirname(os.path.abspath(__file__))
-    for path in sorted(glob.glob(os.path.join(here, "paged_kv_cache_206_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    for name in sorted(seen):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -508,7 +524,7 @@ def measured_traffic(workload, fused, kind="paged_decode"):
                 k, v = line[2:].split(": ", 1)
                 fields[k.strip("` ")] = v.strip().strip("`")
     key = "traffic_bytes_per_call_fused" if fused else "traffic_bytes_per_call_unfused"
-    if fields.get("kernel_source_sha256") != kernel_source_digest() or key not in fields:
+    if fields.get("kernel_source_sha256") != kernel_source_digest(kind) or key not in fields:
         return None
     return int(float(fields[key]))
 
