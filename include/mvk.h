@@ -283,6 +283,8 @@ int32_t mvk_paged_attention_multi_query(void* out, const void* q,
  *                 length <= max_seqlen (host-side bound that sizes the grid).
  *   head_dim 64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
  *   block_size 16. num_seqs == 0 or num_tokens == 0 is a no-op.
+ *   A prompt's rows are addressed with 32-bit byte offsets: (max_seqlen + 256)
+ *   * num_kv_heads * head_dim * 2 above INT32_MAX is MVK_ERR_UNSUPPORTED.
  * Repeated calls give identical bits.
  * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED, MVK_ERR_HIP.
  */

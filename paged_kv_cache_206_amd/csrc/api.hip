@@ -405,6 +405,9 @@ int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const v
   if (num_q_heads % num_kv_heads != 0) return MVK_ERR_INVALID_ARGUMENT;
   if (!mvk::decode_supported(head_dim, num_q_heads / num_kv_heads)) return MVK_ERR_UNSUPPORTED;
   if ((int64_t)num_tokens > (int64_t)num_seqs * max_seqlen) return MVK_ERR_INVALID_ARGUMENT;
+  // a prompt's K/V rows are addressed with 32-bit byte offsets
+  if (((int64_t)max_seqlen + 256) * num_kv_heads * head_dim * 2 > INT32_MAX)
+    return MVK_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return MVK_OK;
   if (!out || !q || !key || !value || !cu_seqlens) return MVK_ERR_INVALID_ARGUMENT;
   if (!aligned16(out) || !aligned16(q) || !aligned16(key) || !aligned16(value) ||

@@ -9,19 +9,37 @@
 // over the prompt's tokens 0..t, and every token's K/V row goes to the slot
 // the block manager gave it (same page, "2. 分页KV缓存（PagedAttention）").
 //
-// Work decomposition: one workgroup of 4 waves per (64 query tokens, query
-// head, prompt); wave w owns 16 of the query tokens, one MFMA tile
-// (attention_mfma.h), for the whole pass, so no wave merges with another.
-// The workgroup walks the prompt's K/V rows from token 0 up to its last query
-// token in tiles of 64 tokens staged in LDS; each wave runs the tile's 16-token
-// blocks below its own causal limit through the MFMA tile, with the limit of
-// every row (token t sees tokens <= t). The K/V rows come from the new
-// key/value tensors (contiguous per prompt), not through the block table:
-// they are this pass's own rows. Later query tiles carry more work and are
-// dispatched first.
+// Work decomposition: one workgroup of W = 4 waves per (32 W query tokens,
+// query head, prompt). Wave w owns two 16-row tiles, query tokens [16w, 16w +
+// 16) and [16W + 16w, 16W + 16w + 16) of the workgroup's range, so the waves reach
+// the causal diagonal at similar depths. The workgroup walks the prompt's K/V
+// rows from token 0 to its last query token in 64-token tiles, double
+// buffered in LDS: the next tile's global loads are in flight while the
+// current one is computed, and one barrier per tile separates the two. The
+// K/V rows come from the new key/value tensors (contiguous per prompt), not
+// through the block table: they are this pass's own rows. Later query ranges
+// carry more work and are dispatched first.
 //
-// LDS rows are padded to D + 8 elements (D*2 + 16 bytes): a 16-row MFMA
-// operand read then touches each of the 64 banks once.
+// Per 32 K/V tokens a wave runs, for each of its tiles:
+//   S^T = K Q^T     two v_mfma_f32_16x16x32 chains (16 tokens x 16 rows each);
+//                   lane l holds tokens 4*(l/16)+i (+16) of row l%16
+//   online softmax  base 2, reference max raised lazily (by more than
+//                   kLazyRescale), masking only on blocks that cross the
+//                   diagonal; p rounded to the storage type (v_cvt_pk_*)
+//   O += P V        v_mfma_f32_16x16x32 with the 32 tokens as the reduction
+//                   index. The 8 p values a lane holds are exactly its
+//                   A-operand slots once the reduction index is ordered
+//                   (tokens 4*q4..4*q4+3, then 16+4*q4..16+4*q4+3) for lane
+//                   group q4; V is stored transposed in LDS in that token
+//                   order, so each B operand is one 16-byte LDS read.
+//   l += P 1        one more MFMA against a ones operand sums the same rounded
+//                   p per row, in the output's own layout.
+// The K/V fragments a wave reads from LDS serve both of its tiles.
+//
+// LDS: the K tile is row-major with rows padded to D + 8 elements (a 16-row
+// operand read touches each bank once); the transposed V tile has rows of
+// kVtPitch = 72 elements, for which the 16 lanes of a 16-byte read also hit
+// distinct banks.
 #include "attention_mfma.h"
 #include "device_common.h"
 #include "launch.h"
@@ -31,12 +49,61 @@ namespace mvk {
 namespace {
 
 constexpr int kPfWaves = 4;
-constexpr int kPfRows = 16 * kPfWaves;  // query tokens per workgroup
+constexpr int kPfRows = 32 * kPfWaves;  // query tokens per workgroup (two tiles per wave)
 constexpr int kPfKvTile = 64;           // K/V tokens per LDS tile
+constexpr int kVtPitch = kPfKvTile + 8;  // transposed-V row pitch, elements
+
+typedef __bf16 pf_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 pf_f16x2_t __attribute__((ext_vector_type(2)));
+typedef float pf_f32x2_t __attribute__((ext_vector_type(2)));
+
+template <int DT> struct PfMath;
+template <> struct PfMath<0> {  // binary16
+  static constexpr uint32_t kOnes = 0x3C003C00u;
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {  // round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(pf_f32x2_t{a, b}, pf_f16x2_t));
+  }
+  static __device__ __forceinline__ f32x4_t mma(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct PfMath<1> {  // bfloat16
+  static constexpr uint32_t kOnes = 0x3F803F80u;
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(pf_f32x2_t{a, b}, pf_bf16x2_t));
+  }
+  static __device__ __forceinline__ f32x4_t mma(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
 
 struct PfShape {
   int32_t num_q_heads, num_kv_heads, num_blocks, query_tiles;
   float scale_log2;
+};
+
+// Position of token t (0..63 of a tile) in a transposed-V row: inside each
+// 32-token half, lane group q4 reads positions 8*q4 .. 8*q4+7, which hold
+// tokens 4*q4..4*q4+3 and 16+4*q4..16+4*q4+3.
+__device__ __forceinline__ int vt_pos(int t) {
+  return 32 * (t >> 5) + 8 * ((t & 15) >> 2) + 4 * ((t >> 4) & 1) + (t & 3);
+}
+
+template <int DT, int D>
+struct PfTile {
+  static constexpr int NKS = D / 32;               // QK reduction steps of 32
+  static constexpr int NE = D / 16;                // PV output column groups
+  static constexpr int kChunks = D / 8;            // 16-byte chunks per row
+  static constexpr int RH = D + 8;                 // K tile pitch, elements
+  static constexpr int kKPerThread = kPfKvTile * kChunks / (kPfWaves * 64);
+  static constexpr int kVUnits = (kPfKvTile / 4) * kChunks;  // (4 tokens x 1 chunk) units
+  static constexpr int kKBytes = kPfKvTile * RH * 2;
+  static constexpr int kVBytes = D * kVtPitch * 2;
+  static constexpr int kBufBytes = kKBytes + kVBytes;
+  static_assert(kKPerThread * kPfWaves * 64 == kPfKvTile * kChunks, "K tile split");
+  static_assert(kVUnits <= kPfWaves * 64, "one V unit per thread at most");
 };
 
 template <int DT, int D, int G>
@@ -46,41 +113,35 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
                     const int32_t* __restrict__ slots, const int32_t* __restrict__ cu_seqlens,
                     PfShape sh) {
-  using Policy = MfmaPolicy<DT, D, 16>;
+  using T = PfTile<DT, D>;
+  using Mth = PfMath<DT>;
   using E = Elem<DT>;
-  constexpr int RH = D + 8;                  // LDS row pitch in 16-bit elements
-  constexpr uint32_t kPitch = RH * 2u;       // ... in bytes
-  constexpr int kChunks = D / 8;             // 16-byte chunks per row
-  constexpr size_t kTileBytes = (size_t)kPfKvTile * RH * 2;
-  constexpr size_t kStateBytes = (size_t)kPfWaves * 16 * D * 4;
-  constexpr size_t kSmem = 2 * kTileBytes > kStateBytes ? 2 * kTileBytes : kStateBytes;
-  // K and V tiles during the pass; each wave's output state after it
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
-  __shared__ float sm_m[kPfWaves][16];
-  __shared__ float sm_l[kPfWaves][16];
-  uint16_t* sk = (uint16_t*)smem;
-  uint16_t* sv = (uint16_t*)(smem + kTileBytes);
-  float* sm_o = (float*)smem;
+  constexpr int NKS = T::NKS, NE = T::NE, RH = T::RH;
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::kBufBytes];
 
   const int s = blockIdx.z;
   const int j = blockIdx.y;                             // query head
-  const int qt = sh.query_tiles - 1 - (int)blockIdx.x;  // latest (heaviest) tiles first
+  const int qt = sh.query_tiles - 1 - (int)blockIdx.x;  // latest (heaviest) ranges first
   const int lo = cu_seqlens[s];
   const int n = cu_seqlens[s + 1] - lo;
   const int q0 = qt * kPfRows;
   if (q0 >= n) return;  // uniform over the workgroup
   const int h = j / G;
   const int Hq = sh.num_q_heads, Hkv = sh.num_kv_heads;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r16 = lane & 15;
+  const int q4 = lane >> 4;
   const int q_end = min(n, q0 + kPfRows);  // the workgroup's query tokens: [q0, q_end)
+  const float sl2 = sh.scale_log2;
 
-  // Cache write: the first query head of each KV head stores this tile's
+  // Cache write: the first query head of each KV head stores the workgroup's
   // tokens' rows of that KV head (every row exactly once over the grid).
   if (slots != nullptr && j % G == 0) {
-    for (int idx = threadIdx.x; idx < (q_end - q0) * kChunks; idx += kPfWaves * 64) {
-      const int t = q0 + idx / kChunks;
-      const int c = idx % kChunks;
+    for (int idx = tid; idx < (q_end - q0) * T::kChunks; idx += kPfWaves * 64) {
+      const int t = q0 + idx / T::kChunks;
+      const int c = idx % T::kChunks;
       const int slot = slots[lo + t];
       if (slot >= 0 && slot < sh.num_blocks * kBlockTokens) {
         const size_t src = ((size_t)(lo + t) * Hkv + h) * D + c * 8;
@@ -91,53 +152,189 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
   }
 
-  // This wave's 16 query tokens; row r16 is token qw0 + r16 and sees tokens
-  // below qw0 + r16 + 1.
-  const int qw0 = q0 + wave * 16;
-  const int r16 = lane & 15;
-  const bool valid = qw0 + r16 < n;
-  Policy pol;
-  pol.init_rows(valid ? q + ((size_t)(lo + qw0 + r16) * Hq + j) * D : nullptr, lane, kPitch);
-  const int row_end = valid ? qw0 + r16 + 1 : 0;
-  const int wave_end = min(n, qw0 + 16);  // no row of this wave sees past this
-
-  for (int kt0 = 0; kt0 < q_end; kt0 += kPfKvTile) {
-    __syncthreads();  // the previous tile has been read
-    for (int idx = threadIdx.x; idx < kPfKvTile * kChunks; idx += kPfWaves * 64) {
-      const int r = idx / kChunks;
-      const int c = idx % kChunks;
-      const int t = kt0 + r;
-      uint4 kk = make_uint4(0u, 0u, 0u, 0u), vv = kk;
-      if (t < q_end) {
-        const size_t src = ((size_t)(lo + t) * Hkv + h) * D + c * 8;
-        kk = *(const uint4*)(key + src);
-        vv = *(const uint4*)(value + src);
-      }
-      *(uint4*)(sk + r * RH + c * 8) = kk;
-      *(uint4*)(sv + r * RH + c * 8) = vv;
-    }
-    __syncthreads();
+  // This wave's two tiles: rows rb[t] + r16 (B operand: row r16's query).
+  int rb[2];
+  uint4 qop[2][NKS];
 #pragma unroll
-    for (int b = 0; b < kPfKvTile / 16; ++b) {
-      const int tok0 = kt0 + 16 * b;
-      if (tok0 >= wave_end) break;  // uniform over the wave
-      typename Policy::Frag f;
-      pol.load_lds(f, (const char*)(sk + 16 * b * RH), (const char*)(sv + 16 * b * RH), kPitch);
-      pol.step(f, tok0, row_end, sh.scale_log2);
+  for (int t = 0; t < 2; ++t) {
+    rb[t] = q0 + 16 * kPfWaves * t + 16 * wave;
+    const int row = rb[t] + r16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qop[t][ks] = row < n ? *(const uint4*)(q + ((size_t)(lo + row) * Hq + j) * D + 32 * ks + 8 * q4)
+                           : make_uint4(0u, 0u, 0u, 0u);
     }
   }
+  f32x4_t acc[2][NE], lacc[2];
+  float m[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[t][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[t] = kNegBig;
+  }
+  const uint4 ones = make_uint4(Mth::kOnes, Mth::kOnes, Mth::kOnes, Mth::kOnes);
 
-  // Each wave normalises and writes its own rows.
-  __syncthreads();  // the last tile has been read: the LDS takes the states
-  pol.to_lds(sm_m[wave], sm_l[wave], sm_o + (size_t)wave * 16 * D);
+  // Staging: K chunk u of this thread is (token idx / kChunks, chunk idx %
+  // kChunks), idx = tid + 256 u; the V unit is tokens 4*vg..4*vg+3 of chunk vc
+  // (token group fastest across lanes, so the transposed writes hit distinct
+  // banks).
+  const int vg = tid & 15;
+  const int vc = tid >> 4;
+  const bool v_owner = vc < T::kChunks;
+  uint4 kreg[T::kKPerThread];
+  uint4 vreg[4];
+  // The prompt's K/V rows through buffer descriptors that end at row q_end:
+  // rows past it read as zero (they are masked anyway), with no branches.
+  const uint32_t row_stride = (uint32_t)Hkv * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(key + (size_t)lo * Hkv * D, (uint32_t)q_end * row_stride);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(value + (size_t)lo * Hkv * D, (uint32_t)q_end * row_stride);
+  const uint32_t head_off = (uint32_t)h * D * 2;
+  auto fetch = [&](int kt0) {
+#pragma unroll
+    for (int u = 0; u < T::kKPerThread; ++u) {
+      const int idx = tid + kPfWaves * 64 * u;
+      const uint32_t t = kt0 + idx / T::kChunks;
+      kreg[u] = buffer_load16(krs, t * row_stride + head_off + 16u * (idx % T::kChunks));
+    }
+    if (v_owner) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t t = kt0 + 4 * vg + r;
+        vreg[r] = buffer_load16(vrs, t * row_stride + head_off + 16u * vc);
+      }
+    }
+  };
+  auto store = [&](int buf) {
+    char* base = smem + buf * T::kBufBytes;
+    uint16_t* sk = (uint16_t*)base;
+#pragma unroll
+    for (int u = 0; u < T::kKPerThread; ++u) {
+      const int idx = tid + kPfWaves * 64 * u;
+      *(uint4*)(sk + (idx / T::kChunks) * RH + 8 * (idx % T::kChunks)) = kreg[u];
+    }
+    if (v_owner) {
+      uint16_t* svt = (uint16_t*)(base + T::kKBytes);
+      const int p = vt_pos(4 * vg);
+      const uint32_t* w0 = (const uint32_t*)&vreg[0];
+      const uint32_t* w1 = (const uint32_t*)&vreg[1];
+      const uint32_t* w2 = (const uint32_t*)&vreg[2];
+      const uint32_t* w3 = (const uint32_t*)&vreg[3];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {  // elements 2k and 2k+1 of the chunk
+        *(uint2*)(svt + (8 * vc + 2 * k) * kVtPitch + p) =
+            make_uint2(__builtin_amdgcn_perm(w1[k], w0[k], kPermLoHalves),
+                       __builtin_amdgcn_perm(w3[k], w2[k], kPermLoHalves));
+        *(uint2*)(svt + (8 * vc + 2 * k + 1) * kVtPitch + p) =
+            make_uint2(__builtin_amdgcn_perm(w1[k], w0[k], kPermHiHalves),
+                       __builtin_amdgcn_perm(w3[k], w2[k], kPermHiHalves));
+      }
+    }
+  };
+
+  const int ntiles = (q_end + kPfKvTile - 1) / kPfKvTile;
+  fetch(0);
+  store(0);
   __syncthreads();
-  const float* so = sm_o + (size_t)wave * 16 * D;
-  for (int idx = lane; idx < 16 * D; idx += 64) {
-    const int rl = idx / D;
-    const int d = idx % D;
-    if (qw0 + rl >= n) break;  // rows are in order: the rest are past the prompt
-    const float l = sm_l[wave][rl];
-    out[((size_t)(lo + qw0 + rl) * Hq + j) * D + d] = E::round(l > 0.0f ? so[idx] / l : 0.0f);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const bool more = kt + 1 < ntiles;
+    if (more) fetch((kt + 1) * kPfKvTile);  // in flight during the compute
+    const char* base = smem + (kt & 1) * T::kBufBytes;
+    const char* sk = base;
+    const char* svt = base + T::kKBytes;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int tok0 = kt * kPfKvTile + 32 * half;
+      bool act[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) act[t] = rb[t] < n && tok0 <= rb[t] + 15;
+      if (act[0] || act[1]) {  // uniform over the wave
+        // K fragments of the two 16-token blocks, V fragments of the 32 tokens
+        uint4 kf[2][NKS], vf[NE];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            kf[b][ks] = *(const uint4*)(sk + (32 * half + 16 * b + r16) * (RH * 2) + 64 * ks +
+                                        16 * q4);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          vf[e] = *(const uint4*)(svt + ((16 * e + r16) * kVtPitch + 32 * half + 8 * q4) * 2);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (!act[t]) continue;
+          f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            s0 = Mth::mma(kf[0][ks], qop[t][ks], s0);
+            s1 = Mth::mma(kf[1][ks], qop[t][ks], s1);
+          }
+          float z[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            z[i] = s0[i];
+            z[4 + i] = s1[i];
+          }
+          if (tok0 + 31 > rb[t]) {  // the 32 tokens cross this tile's diagonal
+            const int lim = rb[t] + r16 + 1;  // row r16 sees tokens below lim
+            const int tb = tok0 + 4 * q4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (tb + i >= lim) z[i] = -INFINITY;
+              if (tb + 16 + i >= lim) z[4 + i] = -INFINITY;
+            }
+          }
+          const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), z[2]),
+                                 fmaxf(fmaxf(fmaxf(z[3], z[4]), z[5]), fmaxf(z[6], z[7]))) * sl2;
+          if (__any(mx > m[t] + kLazyRescale)) {
+            // the 4 lanes of a row (l, l^16, l^32, l^48) agree on its new reference
+            float bm = fmaxf(mx, __shfl_xor(mx, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float mnew = bm > m[t] + kLazyRescale ? bm : m[t];
+            const float alpha = fast_exp2(m[t] - mnew);
+            m[t] = mnew;
+            // output rows 4*q4+i take the factor of the lane that holds row 4*q4+i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float a = __shfl(alpha, 4 * q4 + i);
+              lacc[t][i] *= a;
+#pragma unroll
+              for (int e = 0; e < NE; ++e) acc[t][e][i] *= a;
+            }
+          }
+          const float nm = -m[t];
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(z[i], sl2, nm));
+          const uint4 pa = make_uint4(Mth::pack(p[0], p[1]), Mth::pack(p[2], p[3]),
+                                      Mth::pack(p[4], p[5]), Mth::pack(p[6], p[7]));
+#pragma unroll
+          for (int e = 0; e < NE; ++e) acc[t][e] = Mth::mma(pa, vf[e], acc[t][e]);
+          lacc[t] = Mth::mma(pa, ones, lacc[t]);
+        }
+      }
+    }
+    if (more) store((kt + 1) & 1);  // the other buffer is free since the last barrier
+    __syncthreads();  // the next tile is in LDS; this one may be overwritten
+  }
+
+  // Output rows rb[t] + 4*q4 + i, columns 16e + r16: divided by the row's sum.
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = rb[t] + 4 * q4 + i;
+      if (row < n) {
+        const float inv = 1.0f / lacc[t][i];
+        uint16_t* o = out + ((size_t)(lo + row) * Hq + j) * D + r16;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) o[16 * e] = E::round(acc[t][e][i] * inv);
+      }
+    }
   }
 }
 
@@ -165,8 +362,6 @@ hipError_t launch_prefill_group(const PrefillArgs& a, int group, hipStream_t str
 }
 
 }  // namespace
-
-int32_t prefill_rows_per_workgroup() { return kPfRows; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;

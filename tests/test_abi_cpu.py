@@ -224,6 +224,7 @@ def prefill_call(mvk, **over):
     (dict(vc=FAKE * 5), 1),           # the fused write needs two distinct pools
     (dict(kc=None), 1),
     (dict(nb=0), 1),
+    (dict(maxlen=4_194_304), 2),      # rows past 32-bit byte offsets
 ])
 def test_prefill_validation(mvk, over, status):
     assert prefill_call(mvk, **over) == status
