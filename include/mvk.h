@@ -328,7 +328,9 @@ int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const v
 typedef struct mvk_block_manager mvk_block_manager;
 
 /* A manager of num_blocks blocks of block_size (16) tokens, all free; prefix
- * sharing on when prefix_cache != 0. NULL on bad sizes or no memory. */
+ * sharing on when prefix_cache != 0. NULL on bad sizes (num_blocks must be in
+ * 1 .. INT32_MAX / 16) or no memory. A sequence holds at most INT32_MAX / 2
+ * tokens (MVK_ERR_INVALID_ARGUMENT beyond). */
 mvk_block_manager* mvk_bm_create(int32_t num_blocks, int32_t block_size, int32_t prefix_cache);
 void mvk_bm_destroy(mvk_block_manager* m);
 

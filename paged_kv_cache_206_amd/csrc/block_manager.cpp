@@ -22,6 +22,7 @@
 //  * Slots are flat rows of the pool: slot = block * 16 + offset.
 //  * Rollback drops a sequence's newest tokens (rejected drafts); it never
 //    modifies a block another sequence shares.
+#include <limits.h>
 #include <stdint.h>
 
 #include <list>
@@ -34,6 +35,10 @@
 namespace {
 
 constexpr int32_t kBlock = 16;
+// Sizes stay far from int32 overflow: slots are block * 16 + offset, and
+// token counts are rounded up to whole blocks.
+constexpr int32_t kMaxBlocks = INT32_MAX / kBlock;
+constexpr int32_t kMaxTokens = INT32_MAX / 2;
 
 struct Block {
   int32_t ref = 0;
@@ -181,7 +186,7 @@ struct mvk_block_manager {
 extern "C" {
 
 mvk_block_manager* mvk_bm_create(int32_t num_blocks, int32_t block_size, int32_t prefix_cache) {
-  if (num_blocks <= 0 || block_size != kBlock) return nullptr;
+  if (num_blocks <= 0 || num_blocks > kMaxBlocks || block_size != kBlock) return nullptr;
   return new (std::nothrow) mvk_block_manager(num_blocks, prefix_cache != 0);
 }
 
@@ -193,7 +198,8 @@ int32_t mvk_bm_num_free(const mvk_block_manager* m) {
 
 int32_t mvk_bm_can_admit(const mvk_block_manager* m, const int32_t* token_ids,
                          int32_t num_tokens, int32_t* cached_tokens) {
-  if (!m || num_tokens <= 0 || !token_ids) return MVK_ERR_INVALID_ARGUMENT;
+  if (!m || num_tokens <= 0 || num_tokens > kMaxTokens || !token_ids)
+    return MVK_ERR_INVALID_ARGUMENT;
   int32_t hits, need;
   m->plan(token_ids, num_tokens, &hits, &need);
   if (cached_tokens) *cached_tokens = hits * kBlock;
@@ -202,7 +208,8 @@ int32_t mvk_bm_can_admit(const mvk_block_manager* m, const int32_t* token_ids,
 
 int32_t mvk_bm_admit(mvk_block_manager* m, int64_t seq_id, const int32_t* token_ids,
                      int32_t num_tokens, int32_t* cached_tokens) {
-  if (!m || num_tokens <= 0 || !token_ids) return MVK_ERR_INVALID_ARGUMENT;
+  if (!m || num_tokens <= 0 || num_tokens > kMaxTokens || !token_ids)
+    return MVK_ERR_INVALID_ARGUMENT;
   if (m->seqs.count(seq_id)) return MVK_ERR_INVALID_ARGUMENT;
   int32_t hits, need;
   m->plan(token_ids, num_tokens, &hits, &need);
@@ -233,6 +240,7 @@ int32_t mvk_bm_append(mvk_block_manager* m, int64_t seq_id, int32_t token_id, in
   if (it == m->seqs.end()) return MVK_ERR_INVALID_ARGUMENT;
   Sequence& s = it->second;
   const int32_t pos = (int32_t)s.tokens.size();
+  if (pos >= kMaxTokens) return MVK_ERR_INVALID_ARGUMENT;
   if (pos % kBlock == 0) {  // the last block is full: one more
     if (m->free_queue.empty()) return MVK_ERR_OUT_OF_BLOCKS;
     s.blocks.push_back(m->pop_free());

@@ -277,6 +277,7 @@ def test_invalid_arguments():
     assert bm.block_ref(4) == -1 and bm.block_ref(-1) == -1
     lib = mvk.lib()
     assert lib.mvk_bm_create(4, 32, 1) is None   # only 16-token blocks
+    assert lib.mvk_bm_create(2**31 // 16, 16, 1) is None   # slots would pass int32
     assert lib.mvk_bm_num_free(None) == -1
 
 
