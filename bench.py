@@ -84,7 +84,7 @@ def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the decode path shards by sequence / KV head with no exchange; see DESIGN.md)",
+              "(the decode path would shard by sequence or KV head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 

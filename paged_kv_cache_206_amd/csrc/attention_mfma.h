@@ -102,9 +102,8 @@ struct MfmaPolicy {
     init_rows(r < G ? q + (q_row0 + r) * D : nullptr, lane, row_bytes);
   }
 
-  // kb/vb: wave-uniform address of this KV head's part of token 0 of the
-  // block; every lane adds its fixed offset (scalar base + vector offset)
-  // kr/vr: this KV head's slice of one block; rows past the context read as 0
+  // kr/vr: this KV head's slice of one block (a scalar descriptor; every lane
+  // adds its fixed offset); rows past the context read as 0
   __device__ __forceinline__ void load(Frag& f, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                        uint32_t row_bytes) const {
 #pragma unroll
@@ -114,16 +113,6 @@ struct MfmaPolicy {
       if constexpr (D == 128) f.v[i] = buffer_load16(vr, voff + i * row_bytes);
       else f.v[i] = buffer_load8(vr, voff + i * row_bytes);
     }
-  }
-
-  // The same fragment from a tile in LDS: token rows row_bytes apart, the
-  // same pitch init_rows was given.
-  __device__ __forceinline__ void load_lds(Frag& f, const char* k_tile, const char* v_tile,
-                                           uint32_t row_bytes) const {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) f.k[ks] = *(const uint4*)(k_tile + koff + 64u * ks);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.v[i] = *(const VT*)(v_tile + voff + i * row_bytes);
   }
 
   // Decode: every row slot j < G sees the block's tokens below t_end.

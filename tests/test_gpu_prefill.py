@@ -119,3 +119,43 @@ def test_long_prompt_sampled_rows():
                     for r in rows])
     err = max_err(out[torch.as_tensor(rows, device="cuda")], ref, "f16")
     assert err <= TOL["f16"]
+
+
+def test_empty_prompts_and_a_loose_length_bound():
+    """Zero-length prompts between others write nothing and produce no rows;
+    a max_seqlen above every prompt length only adds workgroups that exit."""
+    pf = W.make_prefill("bf16", [0, 37, 0, 130, 5, 0], 8, 2, 64, seed=8)
+    before_k, before_v = bits(pf.k_cache), bits(pf.v_cache)
+    g = pf.to("cuda")
+    out = mvk.prefill_attention(g.q, g.key, g.value, g.cu_seqlens, g.scale, max_seqlen=600,
+                                k_cache=g.k_cache, v_cache=g.v_cache, slot_mapping=g.slot_mapping)
+    torch.cuda.synchronize()
+    assert max_err(out, oracle_prefill(pf), "bf16") <= TOL["bf16"]
+    k_ref, v_ref = oracle.cache_write(before_k, before_v, bits(pf.key), bits(pf.value),
+                                      pf.slot_mapping.numpy())
+    assert np.array_equal(bits(g.k_cache), k_ref)
+    assert np.array_equal(bits(g.v_cache), v_ref)
+
+
+def test_long_prompt_llama_shape_sampled_rows():
+    """An 8192-token prompt in the Llama-7B shape (32 q / 8 kv heads, head_dim
+    128, bf16): rows on both sides of every kind of boundary (16-row tiles,
+    64-token K/V tiles, 128-token workgroup ranges) and spread over the
+    prompt, each checked against a single-row oracle call over the oracle's
+    own cache write of the prompt."""
+    pf = W.make_prefill("bf16", [8192], 32, 8, 128, seed=9)
+    g = pf.to("cuda")
+    out = gpu_prefill(g)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 8192, 509), [0, 15, 16, 63, 64, 127, 128, 4095,
+                                                               4096, 8063, 8064, 8191]]))
+    q = bits(pf.q)
+    kc, vc = oracle.cache_write(bits(pf.k_cache), bits(pf.v_cache), bits(pf.key), bits(pf.value),
+                                pf.slot_mapping.numpy())
+    bt = pf.block_tables.numpy()
+    ref = np.stack([oracle.paged_multi_query(q[r:r + 1], kc, vc, bt,
+                                             np.array([r + 1], dtype=np.int32),
+                                             np.array([0, 1], dtype=np.int32), pf.scale, "bf16")[0]
+                    for r in rows])
+    err = max_err(out[torch.as_tensor(rows, device="cuda")], ref, "bf16")
+    assert err <= TOL["bf16"]
