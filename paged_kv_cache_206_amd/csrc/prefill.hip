@@ -50,8 +50,6 @@ namespace {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfRows = 32 * kPfWaves;  // query tokens per workgroup (two tiles per wave)
-constexpr int kPfKvTile = 64;           // K/V tokens per LDS tile
-constexpr int kVtPitch = kPfKvTile + 8;  // transposed-V row pitch, elements
 
 typedef __bf16 pf_bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 pf_f16x2_t __attribute__((ext_vector_type(2)));
@@ -84,7 +82,7 @@ struct PfShape {
   float scale_log2;
 };
 
-// Position of token t (0..63 of a tile) in a transposed-V row: inside each
+// Position of token t of a tile in a transposed-V row: inside each
 // 32-token half, lane group q4 reads positions 8*q4 .. 8*q4+7, which hold
 // tokens 4*q4..4*q4+3 and 16+4*q4..16+4*q4+3.
 __device__ __forceinline__ int vt_pos(int t) {
@@ -93,16 +91,18 @@ __device__ __forceinline__ int vt_pos(int t) {
 
 template <int DT, int D>
 struct PfTile {
+  static constexpr int kKvTile = 64;               // K/V tokens per LDS tile
+  static constexpr int kVtPitch = kKvTile + 8;     // transposed-V row pitch, elements
   static constexpr int NKS = D / 32;               // QK reduction steps of 32
   static constexpr int NE = D / 16;                // PV output column groups
   static constexpr int kChunks = D / 8;            // 16-byte chunks per row
   static constexpr int RH = D + 8;                 // K tile pitch, elements
-  static constexpr int kKPerThread = kPfKvTile * kChunks / (kPfWaves * 64);
-  static constexpr int kVUnits = (kPfKvTile / 4) * kChunks;  // (4 tokens x 1 chunk) units
-  static constexpr int kKBytes = kPfKvTile * RH * 2;
+  static constexpr int kKPerThread = kKvTile * kChunks / (kPfWaves * 64);
+  static constexpr int kVUnits = (kKvTile / 4) * kChunks;  // (4 tokens x 1 chunk) units
+  static constexpr int kKBytes = kKvTile * RH * 2;
   static constexpr int kVBytes = D * kVtPitch * 2;
   static constexpr int kBufBytes = kKBytes + kVBytes;
-  static_assert(kKPerThread * kPfWaves * 64 == kPfKvTile * kChunks, "K tile split");
+  static_assert(kKPerThread * kPfWaves * 64 == kKvTile * kChunks, "K tile split");
   static_assert(kVUnits <= kPfWaves * 64, "one V unit per thread at most");
 };
 
@@ -117,6 +117,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   using Mth = PfMath<DT>;
   using E = Elem<DT>;
   constexpr int NKS = T::NKS, NE = T::NE, RH = T::RH;
+  constexpr int kPfKvTile = T::kKvTile, kVtPitch = T::kVtPitch;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::kBufBytes];
 
   const int s = blockIdx.z;
@@ -180,8 +181,9 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   // kChunks), idx = tid + 256 u; the V unit is tokens 4*vg..4*vg+3 of chunk vc
   // (token group fastest across lanes, so the transposed writes hit distinct
   // banks).
-  const int vg = tid & 15;
-  const int vc = tid >> 4;
+  constexpr int kVGroups = kPfKvTile / 4;
+  const int vg = tid % kVGroups;
+  const int vc = tid / kVGroups;
   const bool v_owner = vc < T::kChunks;
   uint4 kreg[T::kKPerThread];
   uint4 vreg[4];
@@ -244,7 +246,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const char* sk = base;
     const char* svt = base + T::kKBytes;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < kPfKvTile / 32; ++half) {  // 32 tokens at a time
       const int tok0 = kt * kPfKvTile + 32 * half;
       bool act[2];
 #pragma unroll
