@@ -233,7 +233,10 @@ int32_t mvk_paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t
  *                 ... <= query_start[num_seqs] = num_query_tokens; every
  *                 n <= max_query_len and n <= L. A sequence with n = 0 has
  *                 no rows. (n > L is not checked on the device: such rows see
- *                 only the positions that exist, or none, and are then zero.)
+ *                 only the positions that exist, or none, and are then zero.
+ *                 Offsets outside [0, num_query_tokens] are clamped into it
+ *                 and n to max_query_len, so inconsistent values give wrong
+ *                 rows but no access outside q, out or the workspace.)
  *   max_query_len host-side bound of n, in [1, 1024].
  *   max_context_len, scale, dtype, partition_tokens: as for decode.
  *   workspace     device scratch of workspace_bytes (from the query above with
@@ -281,6 +284,9 @@ int32_t mvk_paged_attention_multi_query(void* out, const void* q,
  *   cu_seqlens    int32 [num_seqs + 1], on the device: 0 = cu_seqlens[0] <=
  *                 ... <= cu_seqlens[num_seqs] = num_tokens, every prompt
  *                 length <= max_seqlen (host-side bound that sizes the grid).
+ *                 Offsets outside [0, num_tokens] are clamped into it (no
+ *                 access outside the token arrays; rows of a prompt longer
+ *                 than the grid covers are not computed).
  *   head_dim 64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
  *   block_size 16. num_seqs == 0 or num_tokens == 0 is a no-op.
  *   A prompt's rows are addressed with 32-bit byte offsets: (max_seqlen + 256)

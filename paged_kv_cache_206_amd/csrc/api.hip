@@ -373,6 +373,7 @@ int32_t mvk_paged_attention_multi_query(
   a.ws_ml = plan.workspace_bytes ? (float*)workspace : nullptr;
   a.ws_o = plan.workspace_bytes ? (float*)workspace + n_state * 2 : nullptr;
   a.num_seqs = num_seqs;
+  a.num_query_tokens = num_query_tokens;
   a.max_query_len = max_query_len;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -431,6 +432,7 @@ int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const v
   a.slot_mapping = slot_mapping;
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
   a.max_seqlen = max_seqlen;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;

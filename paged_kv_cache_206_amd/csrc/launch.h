@@ -52,7 +52,7 @@ struct MultiQueryArgs {
   const int32_t* query_start;  // [S + 1]: sequence s owns query rows [query_start[s], query_start[s+1])
   float* ws_ml;  // [T, Hq, num_parts, 2] (running max in log2 units, denominator)
   float* ws_o;   // [T, Hq, num_parts, D] normalised partial outputs
-  int32_t num_seqs, max_query_len, num_q_heads, num_kv_heads, head_dim;
+  int32_t num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim;
   int32_t num_blocks, max_blocks_per_seq, max_context_len;
   int32_t partition_tokens, num_parts;
   int32_t tiles;       // 16-row MFMA tiles per workgroup (1, 2, or 4 with head_dim 64)
@@ -73,7 +73,7 @@ struct PrefillArgs {
   void* v_cache;
   const int32_t* slot_mapping;  // [T] or nullptr
   const int32_t* cu_seqlens;    // [S + 1]: prompt s owns rows [cu_seqlens[s], cu_seqlens[s+1])
-  int32_t num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim, num_blocks;
+  int32_t num_seqs, num_tokens, max_seqlen, num_q_heads, num_kv_heads, head_dim, num_blocks;
   float scale_log2;
   int32_t dtype;
 };

@@ -40,9 +40,18 @@ constexpr int kMqMergeThreads = 256;
 
 struct MqShape {
   int32_t num_seqs, num_kv_heads, num_blocks, max_blocks, max_context_len, max_query_len;
-  int32_t partition_tokens, num_parts, row_groups;
+  int32_t partition_tokens, num_parts, row_groups, num_query_tokens;
   float scale_log2;
 };
+
+// Sequence s's query rows [first, first + n): query_start clamped to [0, T]
+// and n to max_query_len, so inconsistent offsets never index outside q, out
+// or the partial states.
+__device__ __forceinline__ void mq_rows(int qs0, int qs1, const MqShape& sh, int& first, int& n) {
+  first = min(max(qs0, 0), sh.num_query_tokens);
+  const int last = min(max(qs1, first), sh.num_query_tokens);
+  n = min(last - first, sh.max_query_len);
+}
 
 // A work item, from the XCD-contiguous item index: row group fastest, then
 // sequence, KV head, partition.
@@ -101,15 +110,16 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
   // Prologue: context length, query range and this wave's table entries
   // (lane k <- block b_begin + wave + k*W) are fetched together.
   const int len = context_lens[s];
-  const int first = query_start[s];
-  const int last = query_start[s + 1];
+  const int qs0 = query_start[s];
+  const int qs1 = query_start[s + 1];
   const int part_blocks = min(P / kBlockTokens, sh.max_blocks - b_begin);
   const int32_t* table = block_tables + (size_t)s * sh.max_blocks;
   int ent = 0;
   if (wave + lane * W < part_blocks) ent = table[b_begin + wave + lane * W];
 
   const int L = min(len, sh.max_context_len);
-  const int n_new = min(max(last - first, 0), sh.max_query_len);
+  int first, n_new;
+  mq_rows(qs0, qs1, sh, first, n_new);
   const int rows = n_new * G;
   const int r0 = it.rg * (NT * kMqRows);
   if (r0 >= rows) return;  // no query rows in this group (uniform over the workgroup)
@@ -228,8 +238,8 @@ __global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
   const int P = sh.partition_tokens;
   const int parts = (L + P - 1) / P;
   if (parts <= 1) return;  // the partition kernel wrote these rows
-  const int first = query_start[s];
-  const int n_new = min(max(query_start[s + 1] - first, 0), sh.max_query_len);
+  int first, n_new;
+  mq_rows(query_start[s], query_start[s + 1], sh, first, n_new);
   const int rows = n_new * G;
   const int r0 = it.rg * (NT * kMqRows);
   if (r0 >= rows) return;
@@ -257,9 +267,9 @@ __global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
 
 template <int DT, int D, int G, int W, int NT>
 hipError_t launch_mq_typed(const MultiQueryArgs& a, hipStream_t stream) {
-  MqShape sh{a.num_seqs,       a.num_kv_heads, a.num_blocks,       a.max_blocks_per_seq,
+  MqShape sh{a.num_seqs,       a.num_kv_heads,  a.num_blocks,       a.max_blocks_per_seq,
              a.max_context_len, a.max_query_len, a.partition_tokens, a.num_parts,
-             a.row_groups,      a.scale_log2};
+             a.row_groups,      a.num_query_tokens, a.scale_log2};
   const int64_t items = (int64_t)a.row_groups * a.num_seqs * a.num_kv_heads * a.num_parts;
   hipLaunchKernelGGL((paged_mq_partition_kernel<DT, D, G, W, NT>), dim3((unsigned)items),
                      dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,

@@ -78,7 +78,7 @@ template <> struct PfMath<1> {  // bfloat16
 };
 
 struct PfShape {
-  int32_t num_q_heads, num_kv_heads, num_blocks, query_tiles;
+  int32_t num_q_heads, num_kv_heads, num_blocks, query_tiles, num_tokens;
   float scale_log2;
 };
 
@@ -123,8 +123,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const int s = blockIdx.z;
   const int j = blockIdx.y;                             // query head
   const int qt = sh.query_tiles - 1 - (int)blockIdx.x;  // latest (heaviest) ranges first
-  const int lo = cu_seqlens[s];
-  const int n = cu_seqlens[s + 1] - lo;
+  // prompt s's rows [lo, lo + n), clamped to [0, T] so that inconsistent
+  // offsets never index outside the token arrays
+  const int lo = min(max(cu_seqlens[s], 0), sh.num_tokens);
+  const int n = min(max(cu_seqlens[s + 1], lo), sh.num_tokens) - lo;
   const int q0 = qt * kPfRows;
   if (q0 >= n) return;  // uniform over the workgroup
   const int h = j / G;
@@ -343,7 +345,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 template <int DT, int D, int G>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   PfShape sh{a.num_q_heads, a.num_kv_heads, a.num_blocks,
-             (a.max_seqlen + kPfRows - 1) / kPfRows, a.scale_log2};
+             (a.max_seqlen + kPfRows - 1) / kPfRows, a.num_tokens, a.scale_log2};
   dim3 grid((unsigned)sh.query_tiles, (unsigned)a.num_q_heads, (unsigned)a.num_seqs);
   hipLaunchKernelGGL((prefill_kernel<DT, D, G>), grid, dim3(kPfWaves * 64), 0, stream,
                      (uint16_t*)a.out, (const uint16_t*)a.q, (const uint16_t*)a.key,
