@@ -130,8 +130,14 @@ def _check(func: str, status: int) -> None:
         raise MvkError(func, status)
 
 
-def _stream(device: torch.device) -> int:
-    return torch.cuda.current_stream(device).cuda_stream
+def _stream(*tensors) -> int:
+    """The current stream of the tensors' device; every tensor given (None
+    skipped) must be on that one device."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t is not None and t.device != dev:
+            raise ValueError(f"all tensors must be on {dev}; found one on {t.device}")
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _require(t: torch.Tensor, name: str, dtype=None, ndim=None):
@@ -172,7 +178,8 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
         raise ValueError("inconsistent shapes")
     st = lib().mvk_reshape_and_cache(key.data_ptr(), value.data_ptr(), k_cache.data_ptr(),
                                     v_cache.data_ptr(), slot_mapping.data_ptr(), T, hkv, d, bs,
-                                    nb, _dtype_code(key), _stream(key.device))
+                                    nb, _dtype_code(key),
+                                    _stream(key, value, k_cache, v_cache, slot_mapping))
     _check("mvk_reshape_and_cache", st)
 
 
@@ -250,7 +257,10 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                           context_lens.data_ptr(), nk, nv, sm, S, hq, hkv, d, bs,
                                           nb, block_tables.shape[1], max_context_len,
                                           float(scale), _dtype_code(q), partition_tokens, ws_ptr,
-                                          ws_bytes, _stream(q.device))
+                                          ws_bytes,
+                                          _stream(q, out, k_cache, v_cache, block_tables,
+                                                  context_lens, new_key, new_value, slot_mapping,
+                                                  workspace))
     _check("mvk_paged_attention_decode", st)
     return out
 
@@ -319,7 +329,8 @@ def paged_attention_multi_query(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), S, T,
         max_query_len, hq, hkv, d, bs, nb, block_tables.shape[1], max_context_len, float(scale),
-        _dtype_code(q), partition_tokens, ws_ptr, ws_bytes, _stream(q.device))
+        _dtype_code(q), partition_tokens, ws_ptr, ws_bytes,
+        _stream(q, out, k_cache, v_cache, block_tables, context_lens, query_start, workspace))
     _check("mvk_paged_attention_multi_query", st)
     return out
 
@@ -368,7 +379,8 @@ def prefill_attention(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
     st = lib().mvk_prefill_attention(out.data_ptr(), q.data_ptr(), key.data_ptr(),
                                      value.data_ptr(), kc, vc, sm, cu_seqlens.data_ptr(), S, T,
                                      max_seqlen, hq, hkv, d, bs, nb, float(scale), _dtype_code(q),
-                                     _stream(q.device))
+                                     _stream(q, out, key, value, cu_seqlens, k_cache, v_cache,
+                                             slot_mapping))
     _check("mvk_prefill_attention", st)
     return out
 

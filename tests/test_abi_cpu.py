@@ -234,3 +234,11 @@ def test_prefill_noop(mvk):
     assert prefill_call(mvk, S=0, T=0, out=None, q=None) == 0
     assert prefill_call(mvk, T=0, out=None, q=None) == 0
 
+
+
+def test_tensors_on_different_devices_are_rejected(mvk):
+    """The binding launches on the current stream of the first tensor's device
+    and refuses a call whose tensors live on different devices."""
+    import torch
+    with pytest.raises(ValueError, match="same|on"):
+        mvk._stream(torch.empty(1), None, torch.empty(1, device="meta"))
