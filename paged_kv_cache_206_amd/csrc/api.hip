@@ -167,7 +167,11 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
                   ? partition_tokens
                   : default_partition((int32_t)(units < INT32_MAX ? units : INT32_MAX),
                                       num_kv_heads, max_context_len);
-  int32_t waves = default_waves(p);
+  // Four waves at every partition length: with two tiles per workgroup the
+  // kernel holds about 230 VGPRs (two waves per SIMD), and eight-wave
+  // workgroups measured slower on long contexts (Llama-7B shape, 4096-token
+  // partitions: 652 vs 623 us with 5 new tokens).
+  int32_t waves = 4;
 #ifdef MVK_TUNING
   if (!partition_tokens && getenv("MVK_TUNE_P")) p = atoi(getenv("MVK_TUNE_P"));
   if (getenv("MVK_TUNE_W")) waves = atoi(getenv("MVK_TUNE_W"));
