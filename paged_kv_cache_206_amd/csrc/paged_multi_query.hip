@@ -222,10 +222,12 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
   }
 }
 
-// One workgroup per (row group, sequence, KV head) whose sequence spans
-// several partitions: out = sum_p w_p o_p / sum_p w_p with
-// w_p = l_p 2^(m_p - max m), over the partitions in index order. A partition
-// that holds none of a row's visible tokens has l_p = 0 and weighs nothing.
+// Workgroups over (row group, sequence, KV head) x chunks of the group's
+// outputs, for sequences that span several partitions; each thread merges one
+// output element, so all of its partition loads are in flight at once:
+// out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - max m), over the
+// partitions in index order. A partition that holds none of a row's visible
+// tokens has l_p = 0 and weighs nothing.
 template <int DT, int D, int G, int NT>
 __global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
@@ -245,7 +247,8 @@ __global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
   if (r0 >= rows) return;
   const int nrow = min(NT * kMqRows, rows - r0);
   const int Hq = sh.num_kv_heads * G;
-  for (int idx = threadIdx.x; idx < nrow * D; idx += kMqMergeThreads) {
+  const int idx = blockIdx.y * kMqMergeThreads + threadIdx.x;
+  if (idx < nrow * D) {
     const int d = idx % D;
     const size_t orow = mq_out_row<G>(first, r0 + idx / D, h, Hq);
     const float* ml = ws_ml + orow * sh.num_parts * 2;
@@ -279,7 +282,8 @@ hipError_t launch_mq_typed(const MultiQueryArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_parts <= 1) return err;
   const int64_t groups = (int64_t)a.row_groups * a.num_seqs * a.num_kv_heads;
-  hipLaunchKernelGGL((paged_mq_merge_kernel<DT, D, G, NT>), dim3((unsigned)groups),
+  const unsigned chunks = (NT * kMqRows * D + kMqMergeThreads - 1) / kMqMergeThreads;
+  hipLaunchKernelGGL((paged_mq_merge_kernel<DT, D, G, NT>), dim3((unsigned)groups, chunks),
                      dim3(kMqMergeThreads), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
                      a.context_lens, a.query_start, sh);
   return hipGetLastError();
