@@ -68,3 +68,78 @@ def test_graph_replay_matches_eager(case, fused):
         torch.cuda.synchronize()
         for a, b in zip(eager, graphed):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (case, rep)
+
+
+def replay_and_check(capture, prepare, pairs, label):
+    """Warm up on a side stream, capture, then replay three times, each after
+    prepare() (clobbering the outputs), unrelated eager work and a sync,
+    comparing every (eager, graphed) pair bit for bit."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        capture()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capture()
+    for rep in range(3):
+        prepare()
+        x = torch.randn(512, 512, device="cuda")
+        (x @ x).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in pairs:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (label, rep)
+
+
+@pytest.mark.parametrize("partition_tokens", [0, 64], ids=["single_pass", "split_merge"])
+def test_multi_query_graph_replay_matches_eager(partition_tokens):
+    lens = [300, 41, 7, 1000, 96]
+    wl = W.make_custom("g", "bf16", lens, 16, 4, 128, sum(-(-L // 16) for L in lens) + 4, 31)
+    q, qs = W.make_queries(wl, [5, 3, 7, 2, 6], seed=32)
+    maxlen, maxq = wl.max_context_len, 7
+    wl, q, qs = wl.to("cuda"), q.to("cuda"), qs.to("cuda")
+    layer = wl.layers[0]
+    nbytes, _ = mvk.multi_query_workspace_size(wl.num_seqs, q.shape[0], maxq, wl.num_q_heads,
+                                               wl.num_kv_heads, wl.head_dim, maxlen,
+                                               partition_tokens)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+
+    def call(out):
+        mvk.paged_attention_multi_query(q, layer.k_cache, layer.v_cache, wl.block_tables,
+                                        wl.context_lens, qs, wl.scale, max_query_len=maxq,
+                                        max_context_len=maxlen, out=out,
+                                        partition_tokens=partition_tokens, workspace=ws)
+    eager = torch.empty_like(q)
+    call(eager)
+    torch.cuda.synchronize()
+    graphed = torch.empty_like(q)
+    replay_and_check(lambda: call(graphed), lambda: graphed.fill_(float("nan")),
+                     [(eager, graphed)], f"mq p={partition_tokens}")
+
+
+def test_prefill_graph_replay_matches_eager():
+    pf = W.make_prefill("f16", [200, 17, 64, 129], 16, 2, 64, seed=33)
+    maxlen = pf.max_seqlen
+    g = pf.to("cuda")
+    k0, v0 = g.k_cache.clone(), g.v_cache.clone()
+
+    def call(out):
+        mvk.prefill_attention(g.q, g.key, g.value, g.cu_seqlens, g.scale, max_seqlen=maxlen,
+                              k_cache=g.k_cache, v_cache=g.v_cache, slot_mapping=g.slot_mapping,
+                              out=out)
+    eager = torch.empty_like(g.q)
+    call(eager)
+    torch.cuda.synchronize()
+    k_eager, v_eager = g.k_cache.clone(), g.v_cache.clone()
+    assert not torch.equal(k_eager.view(torch.int16), k0.view(torch.int16))
+    graphed = torch.empty_like(g.q)
+
+    def prepare():   # the pools as before the call, the output clobbered
+        g.k_cache.copy_(k0)
+        g.v_cache.copy_(v0)
+        graphed.fill_(float("nan"))
+    prepare()
+    replay_and_check(lambda: call(graphed), prepare,
+                     [(eager, graphed), (k_eager, g.k_cache), (v_eager, g.v_cache)], "prefill")
