@@ -166,3 +166,16 @@ def test_long_context_verification_sampled():
     lens = [16384] * 8
     wl, q, qs = mq_case("bf16", lens, [5] * 8, 32, 8, 128, seed=90)
     parity(wl, q, qs, seqs=[0, 3, 5, 7])
+
+
+@pytest.mark.parametrize("g,d,dtype", [(4, 128, "bf16"), (8, 64, "f16")])
+def test_maximum_query_length(g, d, dtype):
+    """1024 new tokens per sequence, the most one call accepts: one sequence
+    entirely new (1024 tokens), one with a 476-token cached prefix, next to a
+    one-token decode row; many row groups per (sequence, KV head); single pass
+    and split."""
+    wl, q, qs = mq_case(dtype, [1500, 1024, 40], [1024, 1024, 1], 2 * g, 2, d, seed=71)
+    parity(wl, q, qs)
+    parity(wl, q, qs, partition_tokens=256)
+    with pytest.raises(mvk.MvkError):   # one more token than a call accepts
+        mvk.multi_query_workspace_size(3, q.shape[0], 1025, 2 * g, 2, d, 1500)
