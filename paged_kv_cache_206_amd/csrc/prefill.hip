@@ -48,8 +48,6 @@ namespace mvk {
 
 namespace {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfRows = 32 * kPfWaves;  // query tokens per workgroup (two tiles per wave)
 
 typedef __bf16 pf_bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 pf_f16x2_t __attribute__((ext_vector_type(2)));
@@ -91,23 +89,26 @@ __device__ __forceinline__ int vt_pos(int t) {
 
 template <int DT, int D>
 struct PfTile {
+  static constexpr int kWaves = 4;                 // waves per workgroup
+  static constexpr int kTiles = 2;                 // 16-row query tiles per wave
+  static constexpr int kRows = 16 * kTiles * kWaves;  // query tokens per workgroup
   static constexpr int kKvTile = 64;               // K/V tokens per LDS tile
   static constexpr int kVtPitch = kKvTile + 8;     // transposed-V row pitch, elements
   static constexpr int NKS = D / 32;               // QK reduction steps of 32
   static constexpr int NE = D / 16;                // PV output column groups
   static constexpr int kChunks = D / 8;            // 16-byte chunks per row
   static constexpr int RH = D + 8;                 // K tile pitch, elements
-  static constexpr int kKPerThread = kKvTile * kChunks / (kPfWaves * 64);
+  static constexpr int kKPerThread = kKvTile * kChunks / (kWaves * 64);
   static constexpr int kVUnits = (kKvTile / 4) * kChunks;  // (4 tokens x 1 chunk) units
   static constexpr int kKBytes = kKvTile * RH * 2;
   static constexpr int kVBytes = D * kVtPitch * 2;
   static constexpr int kBufBytes = kKBytes + kVBytes;
-  static_assert(kKPerThread * kPfWaves * 64 == kKvTile * kChunks, "K tile split");
-  static_assert(kVUnits <= kPfWaves * 64, "one V unit per thread at most");
+  static_assert(kKPerThread * kWaves * 64 == kKvTile * kChunks, "K tile split");
+  static_assert(kVUnits <= kWaves * 64, "one V unit per thread at most");
 };
 
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((PfTile<DT, D>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
                     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
@@ -118,6 +119,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   using E = Elem<DT>;
   constexpr int NKS = T::NKS, NE = T::NE, RH = T::RH;
   constexpr int kPfKvTile = T::kKvTile, kVtPitch = T::kVtPitch;
+  constexpr int kPfWaves = T::kWaves, kPfRows = T::kRows, NT = T::kTiles;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::kBufBytes];
 
   const int s = blockIdx.z;
@@ -156,10 +158,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   }
 
   // This wave's two tiles: rows rb[t] + r16 (B operand: row r16's query).
-  int rb[2];
-  uint4 qop[2][NKS];
+  int rb[NT];
+  uint4 qop[NT][NKS];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NT; ++t) {
     rb[t] = q0 + 16 * kPfWaves * t + 16 * wave;
     const int row = rb[t] + r16;
 #pragma unroll
@@ -168,10 +170,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                            : make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  f32x4_t acc[2][NE], lacc[2];
-  float m[2];
+  f32x4_t acc[NT][NE], lacc[NT];
+  float m[NT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[t][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -250,10 +252,14 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
     for (int half = 0; half < kPfKvTile / 32; ++half) {  // 32 tokens at a time
       const int tok0 = kt * kPfKvTile + 32 * half;
-      bool act[2];
+      bool act[NT];
+      bool any = false;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) act[t] = rb[t] < n && tok0 <= rb[t] + 15;
-      if (act[0] || act[1]) {  // uniform over the wave
+      for (int t = 0; t < NT; ++t) {
+        act[t] = rb[t] < n && tok0 <= rb[t] + 15;
+        any = any || act[t];
+      }
+      if (any) {  // uniform over the wave
         // K fragments of the two 16-token blocks, V fragments of the 32 tokens
         uint4 kf[2][NKS], vf[NE];
 #pragma unroll
@@ -269,7 +275,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
           vf[e] = *(const uint4*)(svt + ((16 * e + r16) * kVtPitch + 32 * half + 8 * q4) * 2);
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NT; ++t) {
           if (!act[t]) continue;
           f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
@@ -328,7 +334,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 
   // Output rows rb[t] + 4*q4 + i, columns 16e + r16: divided by the row's sum.
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = rb[t] + 4 * q4 + i;
@@ -344,10 +350,11 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 
 template <int DT, int D, int G>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
+  using T = PfTile<DT, D>;
   PfShape sh{a.num_q_heads, a.num_kv_heads, a.num_blocks,
-             (a.max_seqlen + kPfRows - 1) / kPfRows, a.num_tokens, a.scale_log2};
+             (a.max_seqlen + T::kRows - 1) / T::kRows, a.num_tokens, a.scale_log2};
   dim3 grid((unsigned)sh.query_tiles, (unsigned)a.num_q_heads, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((prefill_kernel<DT, D, G>), grid, dim3(kPfWaves * 64), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<DT, D, G>), grid, dim3(T::kWaves * 64), 0, stream,
                      (uint16_t*)a.out, (const uint16_t*)a.q, (const uint16_t*)a.key,
                      (const uint16_t*)a.value, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache,
                      a.slot_mapping, a.cu_seqlens, sh);
