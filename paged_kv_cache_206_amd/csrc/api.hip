@@ -121,7 +121,9 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   plan->use_counters = parts > 1 && merge_in_kernel &&
                        (size_t)num_seqs * num_kv_heads * 4u <= kCounterRegion;
   plan->workspace_bytes = plan->counter_bytes + plan->partial_bytes +
-                          (plan->work_list ? (size_t)(1 + 2 * num_seqs * parts) * 4u : 0);
+                          (plan->work_list
+                               ? (size_t)(1 + num_kv_heads + 2 * num_seqs * parts) * 4u
+                               : 0);
   return MVK_OK;
 }
 

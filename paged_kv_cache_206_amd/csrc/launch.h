@@ -29,7 +29,8 @@ struct DecodeArgs {
   int32_t partition_tokens, num_parts;
   int32_t waves;     // waves per workgroup (4 or 8)
   int32_t head_fastest;  // grid order (see Shape)
-  int32_t* items;    // work list (count, then (seq, part) pairs); nullptr = grid mode
+  int32_t* items;    // work list (count, one dispatch counter per KV head, then (seq, part)
+                     // pairs); nullptr = grid mode
   int32_t* counters; // per (seq, KV head) partition counters (zero between calls), or
                      // nullptr: partitions are merged by a separate kernel
   int32_t list_workgroups;  // workgroups per KV head in work-list mode

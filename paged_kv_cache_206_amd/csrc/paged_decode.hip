@@ -419,13 +419,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMinWave
     uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
     uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ items, Shape sh,
+    const int32_t* __restrict__ context_lens, int32_t* __restrict__ items, Shape sh,
     const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value,
     const int32_t* __restrict__ slots, int32_t* __restrict__ counters) {
   __shared__ float sm_o[W][G * D];
   __shared__ float sm_m[W][G];
   __shared__ float sm_l[W][G];
   __shared__ int sm_last;
+  __shared__ int sm_claim;            // work-list mode: the item this workgroup claimed
   __shared__ uint4 sm_new[2][D / 8];  // the step's new K and V row (fused write)
   if (items == nullptr) {
     // Workgroups are dealt round-robin to the 8 XCDs in dispatch order; remap
@@ -445,10 +446,18 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMinWave
                                                &sm_last, sm_new[0], sm_new[1]);
     return;
   }
+  // Claim items one at a time through this KV head's dispatch counter; every
+  // workgroup stops at its first claim past the end of the list.
   const int count = items[0];
-  for (int i = blockIdx.x; i < count; i += gridDim.x) {
-    const int s = items[1 + 2 * i];
-    const int part = items[2 + 2 * i];
+  int32_t* next = items + 1 + blockIdx.y;
+  const int32_t* pairs = items + 1 + sh.num_kv_heads;
+  for (;;) {
+    if (threadIdx.x == 0) sm_claim = atomicAdd(next, 1);
+    __syncthreads();
+    const int i = sm_claim;
+    if (i >= count) break;  // uniform over the workgroup
+    const int s = pairs[2 * i];
+    const int part = pairs[2 * i + 1];
     decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache,
                                                v_cache, block_tables, context_lens, sh, new_key,
                                                new_value, slots, counters, sm_o, sm_m, sm_l,
@@ -457,46 +466,63 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMinWave
   }
 }
 
-// Work list for work-list mode: items[0] = count, then (sequence, partition)
-// pairs in sequence order, one per partition that holds context tokens (one
-// partition for an empty context, which writes its zero row). One workgroup
-// of kPlanThreads threads: each thread counts a contiguous range of
-// sequences, a workgroup-wide exclusive scan gives every thread its output
-// offset, then each thread writes its own items.
+// Work list for work-list mode: items[0] = count, items[1 .. Hkv] = one
+// dispatch counter per KV head (reset here), then (sequence, partition)
+// pairs, one per partition that holds context tokens (one partition for an
+// empty context, which writes its zero row). Full partitions (every one but
+// a sequence's last) come first, then the last partitions, each group in
+// sequence order. Workgroups claim items through the counters, so the
+// longest items start first and each later item goes to whichever
+// workgroup is free (list scheduling). One workgroup of kPlanThreads
+// threads: each thread counts both kinds over a contiguous range of
+// sequences, workgroup-wide exclusive scans give every thread its two output
+// offsets, then each thread writes its own items.
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void paged_decode_plan_kernel(
     int32_t* __restrict__ items, const int32_t* __restrict__ context_lens, int32_t num_seqs,
-    int32_t max_context_len, int32_t partition_tokens) {
-  __shared__ int32_t sums[kPlanThreads];
+    int32_t num_kv_heads, int32_t max_context_len, int32_t partition_tokens) {
+  __shared__ int32_t sums_full[kPlanThreads];
+  __shared__ int32_t sums_last[kPlanThreads];
   const int t = threadIdx.x;
   const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(t * per, num_seqs);
   const int s1 = min(s0 + per, num_seqs);
-  int n = 0;
-  for (int s = s0; s < s1; ++s) {
+  auto parts_of = [&](int s) {
     const int L = min(context_lens[s], max_context_len);
-    n += L > 0 ? (L + partition_tokens - 1) / partition_tokens : 1;
-  }
-  sums[t] = n;
+    return L > 0 ? (L + partition_tokens - 1) / partition_tokens : 1;
+  };
+  int n_full = 0;
+  for (int s = s0; s < s1; ++s) n_full += parts_of(s) - 1;
+  const int n_last = s1 - s0;
+  sums_full[t] = n_full;
+  sums_last[t] = n_last;
   __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread counts
+  // Hillis-Steele inclusive scans over the per-thread counts
   for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int v = t >= off ? sums[t - off] : 0;
+    const int vf = t >= off ? sums_full[t - off] : 0;
+    const int vl = t >= off ? sums_last[t - off] : 0;
     __syncthreads();
-    sums[t] += v;
+    sums_full[t] += vf;
+    sums_last[t] += vl;
     __syncthreads();
   }
-  int pos = sums[t] - n;
+  const int total_full = sums_full[kPlanThreads - 1];
+  int pos_full = sums_full[t] - n_full;
+  int pos_last = total_full + sums_last[t] - n_last;
+  int32_t* pairs = items + 1 + num_kv_heads;
   for (int s = s0; s < s1; ++s) {
-    const int L = min(context_lens[s], max_context_len);
-    const int parts = L > 0 ? (L + partition_tokens - 1) / partition_tokens : 1;
-    for (int p = 0; p < parts; ++p, ++pos) {
-      items[1 + 2 * pos] = s;
-      items[2 + 2 * pos] = p;
+    const int parts = parts_of(s);
+    for (int p = 0; p + 1 < parts; ++p, ++pos_full) {
+      pairs[2 * pos_full] = s;
+      pairs[2 * pos_full + 1] = p;
     }
+    pairs[2 * pos_last] = s;
+    pairs[2 * pos_last + 1] = parts - 1;
+    ++pos_last;
   }
-  if (t == kPlanThreads - 1) items[0] = sums[t];
+  for (int h = t; h < num_kv_heads; h += kPlanThreads) items[1 + h] = 0;
+  if (t == kPlanThreads - 1) items[0] = total_full + sums_last[t];
 }
 
 // Merge the partitions of every (sequence, KV head) whose context spans more
@@ -584,7 +610,8 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_parts);
   if (a.items != nullptr) {
     hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.items,
-                       a.context_lens, a.num_seqs, a.max_context_len, a.partition_tokens);
+                       a.context_lens, a.num_seqs, a.num_kv_heads, a.max_context_len,
+                       a.partition_tokens);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     grid = dim3((unsigned)a.list_workgroups, (unsigned)a.num_kv_heads, 1u);
@@ -592,7 +619,7 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, W, NPF, USE_MFMA, FUSED>), grid,
                      dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
                      (const uint16_t*)a.q, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache,
-                     a.block_tables, a.context_lens, (const int32_t*)a.items, sh,
+                     a.block_tables, a.context_lens, a.items, sh,
                      (const uint16_t*)a.new_key, (const uint16_t*)a.new_value, a.slot_mapping,
                      a.counters);
   hipError_t err = hipGetLastError();

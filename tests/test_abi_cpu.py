@@ -142,7 +142,7 @@ def test_workspace_size(mvk):
     # skewed batch: the dense grid would be huge, so a work list is appended
     nbytes, p = mvk.workspace_size(512, 16, 8, 128, 131072, 1024)
     parts = 131072 // 1024
-    assert nbytes == 65536 + 512 * 16 * parts * 130 * 4 + (1 + 2 * 512 * parts) * 4
+    assert nbytes == 65536 + 512 * 16 * parts * 130 * 4 + (1 + 8 + 2 * 512 * parts) * 4
     with pytest.raises(mvk.MvkError):
         mvk.workspace_size(2, 3, 2, 64, 10)
 
