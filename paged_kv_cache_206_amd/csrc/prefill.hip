@@ -123,9 +123,17 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   constexpr int kPfWaves = T::kWaves, kPfRows = T::kRows, NT = T::kTiles;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::kBufBytes];
 
-  const int s = blockIdx.z;
-  const int j = blockIdx.y;                             // query head
-  const int qt = sh.query_tiles - 1 - (int)blockIdx.x;  // latest (heaviest) ranges first
+  // Workgroups are dealt round-robin to the XCDs in dispatch order; remap so
+  // that each XCD runs whole (query head, prompt) groups. Their query ranges
+  // then share K/V tiles in one L2, and every XCD gets the same mix of heavy
+  // and light ranges (with the range index fastest and no remap, XCD k would
+  // get ranges k and k + 8 of every group: 2.4x more work on some XCDs).
+  const uint32_t n_wg = gridDim.x * gridDim.y * gridDim.z;
+  const uint32_t v =
+      xcd_contiguous(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), n_wg);
+  const int s = v / (gridDim.x * gridDim.y);
+  const int j = (v / gridDim.x) % gridDim.y;                // query head
+  const int qt = sh.query_tiles - 1 - (int)(v % gridDim.x);  // latest (heaviest) ranges first
   // prompt s's rows [lo, lo + n), clamped to [0, T] so that inconsistent
   // offsets never index outside the token arrays
   const int lo = min(max(cu_seqlens[s], 0), sh.num_tokens);
