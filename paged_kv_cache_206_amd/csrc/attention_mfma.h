@@ -65,8 +65,13 @@ struct MfmaPolicy {
   static constexpr int NE = VW;       // PV products (16 output columns each)
   using VT = typename std::conditional<D == 128, uint4, uint2>::type;
 
+  // K is loaded in whole 128-byte lines and rearranged (arrange) into the
+  // QK operand layout: operand ks of lane l is K[token l%16][32*ks + 8*(l/16)
+  // .. +7]. Load 2*h+T of lane l reads token 8*T + l%8, 16-byte chunk
+  // 8*h + l/16 + 4*((l%16)/8) of the row: each instruction covers line h of
+  // 8 token rows.
   struct Frag {
-    uint4 k[NKS];  // K[token l%16][32*ks + 8*(l/16) .. +7]
+    uint4 k[NKS];  // as loaded; after arrange(), the QK operands
     VT v[4];       // V[token 4*(l/16)+i][VW*(l%16) .. +VW-1]
   };
 
@@ -82,7 +87,7 @@ struct MfmaPolicy {
   __device__ __forceinline__ void init_rows(const uint16_t* q_row, int lane, uint32_t row_bytes) {
     r16 = lane & 15;
     q4 = lane >> 4;
-    koff = r16 * row_bytes + 16u * q4;
+    koff = (lane & 7) * row_bytes + 16u * (q4 + 4 * ((lane & 15) >> 3));
     voff = 4u * q4 * row_bytes + 2u * VW * r16;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -107,11 +112,28 @@ struct MfmaPolicy {
   __device__ __forceinline__ void load(Frag& f, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                        uint32_t row_bytes) const {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) f.k[ks] = buffer_load16(kr, koff + 64u * ks);
+    for (int ks = 0; ks < NKS; ++ks) {
+      f.k[ks] = buffer_load16<kStreamLoad>(kr, koff + 128u * (ks >> 1) + 8u * (ks & 1) * row_bytes);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (D == 128) f.v[i] = buffer_load16(vr, voff + i * row_bytes);
-      else f.v[i] = buffer_load8(vr, voff + i * row_bytes);
+      if constexpr (D == 128) f.v[i] = buffer_load16<kStreamLoad>(vr, voff + i * row_bytes);
+      else f.v[i] = buffer_load8<kStreamLoad>(vr, voff + i * row_bytes);
+    }
+  }
+
+  // Loaded K lines -> QK operands. For line h, load A = k[2h] holds tokens
+  // 0-7 and B = k[2h+1] tokens 8-15; operand 2h takes A's first half-row and
+  // B's chunks from 8 lanes away, operand 2h+1 the reverse.
+  __device__ __forceinline__ void arrange(Frag& f) const {
+#pragma unroll
+    for (int h = 0; h < NKS / 2; ++h) {
+      const uint4 a = f.k[2 * h], b = f.k[2 * h + 1];
+      f.k[2 * h] = make_uint4(swap_half_rows<kDppBanksHi>(a.x, b.x), swap_half_rows<kDppBanksHi>(a.y, b.y),
+                              swap_half_rows<kDppBanksHi>(a.z, b.z), swap_half_rows<kDppBanksHi>(a.w, b.w));
+      f.k[2 * h + 1] =
+          make_uint4(swap_half_rows<kDppBanksLo>(b.x, a.x), swap_half_rows<kDppBanksLo>(b.y, a.y),
+                     swap_half_rows<kDppBanksLo>(b.z, a.z), swap_half_rows<kDppBanksLo>(b.w, a.w));
     }
   }
 
@@ -119,6 +141,7 @@ struct MfmaPolicy {
   // nk/nv: the step's new K/V row of this KV head in LDS, as 16-byte chunks
   __device__ __forceinline__ void process(Frag& f, int tok0, int t_end, float scale_log2, bool sub,
                                           const uint4* nk, const uint4* nv) {
+    arrange(f);
     if (sub) {  // this block holds the new row: take it from LDS, not memory
       if (r16 == row_new) {
 #pragma unroll
@@ -132,8 +155,9 @@ struct MfmaPolicy {
     step(f, tok0, r16 < G ? t_end : 0, scale_log2);
   }
 
-  // One block of 16 tokens starting at tok0; this lane's row slot r16 sees
-  // the tokens below row_end (its own limit: causal masks differ per row).
+  // One block of 16 tokens starting at tok0 (K already arranged); this lane's
+  // row slot r16 sees the tokens below row_end (its own limit: causal masks
+  // differ per row).
   __device__ __forceinline__ void step(Frag& f, int tok0, int row_end, float scale_log2) {
     using M = Mma<DT>;
     using E = Elem<DT>;

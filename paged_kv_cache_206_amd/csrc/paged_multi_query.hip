@@ -175,6 +175,7 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
       for (int j = 0; j < NPF; ++j) {
         const int k = k0 + j;
         load_block(f[(j + NPF - 1) % NPF], k + NPF - 1);
+        pol[0].arrange(f[j]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) pol[t].step(f[j], tok_of(k), row_end[t], sh.scale_log2);
         if (k + 1 >= my_blocks) goto blocks_done;
