@@ -85,10 +85,10 @@ def test_partition_boundaries_inside_the_new_tokens(p):
     assert diff <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("dtype,d,g", [("f16", 64, 8), ("bf16", 128, 4)])
+@pytest.mark.parametrize("dtype,d,g", [("f16", 64, 8), ("bf16", 128, 4), ("bf16", 128, 2)])
 def test_one_new_token_equals_decode_bitwise(dtype, d, g):
     """With n = 1 everywhere the rows are the decode call's rows; on the MFMA
-    shapes (g >= 4) the arithmetic is the same, so the bits are too."""
+    shapes (g >= 2) the arithmetic is the same, so the bits are too."""
     lens = [1, 30, 64, 17, 250, 2]
     wl, q, qs = mq_case(dtype, lens, [1] * len(lens), 2 * g, 2, d, seed=50 + g)
     wl.layers[0].q = q
