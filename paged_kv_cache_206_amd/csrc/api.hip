@@ -22,6 +22,9 @@ constexpr int32_t kMaxGridYZ = 65535;
 // grid would be partitions past short contexts, each costing a dispatch and a
 // load only to exit.
 constexpr int64_t kGridLimit = 16384;
+// Shortest longest-context (tokens) for which a single-pass grid is
+// dispatched longest sequence first.
+constexpr int32_t kMinOrderedContext = 1024;
 // Workgroups (over all KV heads) that walk the work list.
 constexpr int64_t kListWorkgroups = 4096;
 // Any workspace starts with this many bytes of partition counters, one int32
@@ -66,6 +69,7 @@ struct Plan {
   int32_t num_parts;
   int32_t waves;
   int32_t head_fastest;
+  int32_t longest_first;
   bool work_list;
   int32_t list_workgroups;
   size_t counter_bytes;    // the counter region at the start of the workspace
@@ -108,6 +112,14 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
       parts > 1 ? (size_t)num_seqs * num_q_heads * (size_t)parts * (size_t)(head_dim + 2) * 4u : 0;
   const int64_t dense = (int64_t)num_seqs * parts * num_kv_heads;
   plan->work_list = parts > 1 && dense > kGridLimit;
+  // One partition per sequence, a batch the decode kernel can rank in every
+  // workgroup (at most 256 sequences), and contexts long enough that the
+  // ranking's extra memory round trip at the start of every workgroup
+  // (about 1.5 us) is repaid: dispatch longest first. Measured on MI355X:
+  // 256 x 4 items of 512-2048 tokens 71.5 -> 68.6 us; 60 x 8 items of
+  // 64-256 tokens 11.2 -> 12.1 us (so short contexts keep batch order).
+  plan->longest_first = parts == 1 && num_seqs <= mvk::kMaxOrderedSeqs &&
+                        max_context_len >= kMinOrderedContext && !head_fastest;
   if (!plan->work_list && dense > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
   const int64_t per_head = (kListWorkgroups + num_kv_heads - 1) / num_kv_heads;
   plan->list_workgroups = (int32_t)(per_head < num_seqs * parts ? per_head : num_seqs * parts);
@@ -315,6 +327,7 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
   a.num_parts = plan.num_parts;
   a.waves = plan.waves;
   a.head_fastest = plan.head_fastest;
+  a.longest_first = plan.longest_first;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;
   hipError_t err = mvk::launch_paged_decode(a, (hipStream_t)stream);

@@ -12,6 +12,10 @@ hipError_t launch_cache_write(const void* key, const void* value, void* k_cache,
                               const int32_t* slot_mapping, int32_t num_tokens, int32_t row_vecs,
                               int64_t num_slots, hipStream_t stream);
 
+// Largest batch whose single-pass decode grid is dispatched longest sequence
+// first (the decode kernel ranks the batch's sequences in every workgroup).
+constexpr int32_t kMaxOrderedSeqs = 256;
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -29,6 +33,7 @@ struct DecodeArgs {
   int32_t partition_tokens, num_parts;
   int32_t waves;     // waves per workgroup (4 or 8)
   int32_t head_fastest;  // grid order (see Shape)
+  int32_t longest_first; // single-pass grid dispatched longest sequence first (see Shape)
   int32_t* items;    // work list (count, one dispatch counter per KV head, then (seq, part)
                      // pairs); nullptr = grid mode
   int32_t* counters; // per (seq, KV head) partition counters (zero between calls), or

@@ -215,3 +215,28 @@ def test_workspace_reused_across_calls():
                                              partition_tokens=p, workspace=ws)
             torch.cuda.synchronize()
             assert max_err(out, ref, "bf16") <= TOL["bf16"], (rnd, p)
+
+
+@pytest.mark.parametrize("num_seqs", [1, 2, 63, 64, 65, 200, 256, 257])
+@pytest.mark.parametrize("dtype,d,g", [("bf16", 128, 2), ("f16", 64, 8)])
+def test_longest_first_order_writes_every_row(num_seqs, dtype, d, g):
+    """Single-pass grids of up to 256 sequences are dispatched longest sequence
+    first, each workgroup ranking the batch itself; every (sequence, head) row
+    must be written exactly once with the right value, whatever the ties (many
+    equal lengths, empty contexts) and whether or not the batch is ranked
+    (257 sequences is not). `out` starts as NaN, so a row no workgroup writes
+    fails the finiteness check."""
+    rng = np.random.default_rng(num_seqs * 10 + g)
+    # the longest context is 1100 tokens: the batch is ranked (up to 256 sequences)
+    lens = [int(x) for x in rng.choice([0, 1, 16, 17, 100, 100, 100, 250, 250, 1100], size=num_seqs)]
+    lens[0] = 1100
+    wl = custom(dtype, lens, 2 * g, 2, d, seed=num_seqs + g)
+    print(f"longest-first S={num_seqs} {dtype} d={d} g={g}", flush=True)
+    wl_gpu = wl.to("cuda")
+    layer = wl_gpu.layers[0]
+    out = torch.full_like(layer.q, float("nan"))
+    gpu_decode(wl_gpu, partition_tokens=4096, out=out)
+    torch.cuda.synchronize()
+    ref = oracle_decode(wl)
+    err = max_err(out, ref, wl.dtype)
+    assert err <= TOL[wl.dtype], f"max abs err {err:.3e} > {TOL[wl.dtype]}"
