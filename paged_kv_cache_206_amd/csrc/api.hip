@@ -152,6 +152,7 @@ struct MqPlan {
   int32_t waves;
   int32_t tiles;           // 16-row tiles per workgroup
   int32_t row_groups;      // workgroups per (sequence, KV head, partition)
+  int32_t longest_first;   // as in decode: single pass, <= 256 sequences, long contexts
   size_t workspace_bytes;  // partial (m, l, o) states, when sequences are split
 };
 
@@ -200,6 +201,11 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
   plan->waves = waves;
   plan->tiles = tiles;
   plan->row_groups = row_groups;
+  // Row groups of one (sequence, KV head) read the same blocks: in the
+  // XCD-contiguous order they share an L2, in longest-first order they would
+  // not, so several row groups keep that order.
+  plan->longest_first = parts == 1 && row_groups == 1 && num_seqs <= mvk::kMaxOrderedSeqs &&
+                        max_context_len >= kMinOrderedContext;
   plan->workspace_bytes = parts > 1 ? (size_t)num_query_tokens * num_q_heads * (size_t)parts *
                                           (size_t)(head_dim + 2) * 4u
                                     : 0;
@@ -404,6 +410,7 @@ int32_t mvk_paged_attention_multi_query(
   a.num_parts = plan.num_parts;
   a.tiles = plan.tiles;
   a.row_groups = plan.row_groups;
+  a.longest_first = plan.longest_first;
   a.waves = plan.waves;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;

@@ -64,6 +64,7 @@ struct MultiQueryArgs {
   int32_t tiles;       // 16-row MFMA tiles per workgroup (1, 2, or 4 with head_dim 64)
   int32_t row_groups;  // groups of 16 * tiles (new token, query head) rows per (sequence, KV head)
   int32_t waves;       // waves per workgroup (4 or 8)
+  int32_t longest_first;  // single-pass grid dispatched longest sequence first
   float scale_log2;
   int32_t dtype;
 };

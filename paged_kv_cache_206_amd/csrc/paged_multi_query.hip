@@ -29,6 +29,7 @@
 #include "attention_mfma.h"
 #include "device_common.h"
 #include "launch.h"
+#include "ordering.h"
 
 namespace mvk {
 
@@ -42,6 +43,7 @@ struct MqShape {
   int32_t num_seqs, num_kv_heads, num_blocks, max_blocks, max_context_len, max_query_len;
   int32_t partition_tokens, num_parts, row_groups, num_query_tokens;
   float scale_log2;
+  int32_t longest_first;  // single-pass grid dispatched longest sequence first (ordering.h)
 };
 
 // Sequence s's query rows [first, first + n): query_start clamped to [0, T]
@@ -98,7 +100,18 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
   __shared__ float sm_m[W][kMqRows];
   __shared__ float sm_l[W][kMqRows];
 
-  const MqItem it = mq_item(xcd_contiguous(blockIdx.x, gridDim.x), sh);
+  MqItem it;
+  if (sh.longest_first) {  // (row group fastest, KV head, sequence rank), one partition
+    const uint32_t i = blockIdx.x;
+    it.rg = i % sh.row_groups;
+    it.h = (i / sh.row_groups) % sh.num_kv_heads;
+    it.part = 0;
+    it.s = __builtin_amdgcn_readfirstlane(sequence_of_rank(
+        context_lens, sh.num_seqs, (int)(i / ((uint32_t)sh.row_groups * sh.num_kv_heads)),
+        sh.max_context_len));
+  } else {
+    it = mq_item(xcd_contiguous(blockIdx.x, gridDim.x), sh);
+  }
   const int s = it.s, h = it.h, part = it.part;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -273,7 +286,7 @@ template <int DT, int D, int G, int W, int NT>
 hipError_t launch_mq_typed(const MultiQueryArgs& a, hipStream_t stream) {
   MqShape sh{a.num_seqs,       a.num_kv_heads,  a.num_blocks,       a.max_blocks_per_seq,
              a.max_context_len, a.max_query_len, a.partition_tokens, a.num_parts,
-             a.row_groups,      a.num_query_tokens, a.scale_log2};
+             a.row_groups,      a.num_query_tokens, a.scale_log2, a.longest_first};
   const int64_t items = (int64_t)a.row_groups * a.num_seqs * a.num_kv_heads * a.num_parts;
   hipLaunchKernelGGL((paged_mq_partition_kernel<DT, D, G, W, NT>), dim3((unsigned)items),
                      dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,

@@ -179,3 +179,27 @@ def test_maximum_query_length(g, d, dtype):
     parity(wl, q, qs, partition_tokens=256)
     with pytest.raises(mvk.MvkError):   # one more token than a call accepts
         mvk.multi_query_workspace_size(3, q.shape[0], 1025, 2 * g, 2, d, 1500)
+
+
+@pytest.mark.parametrize("num_seqs", [1, 65, 256, 257])
+@pytest.mark.parametrize("dtype,d,g", [("f16", 64, 8), ("bf16", 128, 2)])
+def test_longest_first_order_writes_every_row(num_seqs, dtype, d, g):
+    """Single-pass multi-query grids of up to 256 sequences with one row group
+    and a longest context of at least 1024 tokens are dispatched longest
+    sequence first (each workgroup ranks the batch); every row must be written
+    once with the right value whatever the ties and empty contexts (257
+    sequences keep batch order). `out` starts as NaN, so an unwritten row fails."""
+    rng = np.random.default_rng(num_seqs * 7 + g)
+    lens = [int(x) for x in rng.choice([0, 3, 16, 17, 100, 100, 250, 1100], size=num_seqs)]
+    lens[0] = 1100
+    news = [min(L, int(rng.integers(0, 3))) for L in lens]
+    news[0] = 2
+    wl, q, qs = mq_case(dtype, lens, news, 2 * g, 2, d, seed=num_seqs + g)
+    print(f"mq longest-first S={num_seqs} {dtype} d={d} g={g}", flush=True)
+    wl_gpu = wl.to("cuda")
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    gpu_mq(wl_gpu, q.to("cuda"), qs.to("cuda"), partition_tokens=4096, out=out)
+    torch.cuda.synchronize()
+    ref, _ = oracle_mq(wl, q, qs)
+    err = max_err(out, ref, wl.dtype)
+    assert err <= TOL[wl.dtype], f"max abs err {err:.3e} > {TOL[wl.dtype]}"
