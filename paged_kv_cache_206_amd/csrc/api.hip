@@ -22,6 +22,9 @@ constexpr int32_t kMaxGridYZ = 65535;
 // grid would be partitions past short contexts, each costing a dispatch and a
 // load only to exit.
 constexpr int64_t kGridLimit = 16384;
+// Partition length (tokens) the library chooses for batches that run in
+// work-list mode.
+constexpr int32_t kWorkListPartition = 3072;
 // Shortest longest-context (tokens) for which a single-pass grid is
 // dispatched longest sequence first.
 constexpr int32_t kMinOrderedContext = 1024;
@@ -91,6 +94,17 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   int32_t p = partition_tokens ? partition_tokens
                                : default_partition(num_seqs, num_kv_heads, max_context_len);
   int32_t waves = default_waves(p);
+  if (!partition_tokens && p == kMaxPartition) {
+    // A batch whose dense grid at the longest partitions would run in
+    // work-list mode (a few very long sequences among many short ones) takes
+    // 3072-token partitions, with the same 8 waves. Measured on MI355X, 512
+    // sequences up to 131072 tokens: 4096-token partitions 362.6 us, 3072
+    // 351.5 us, 2048 374 us (the longest sequence's items are then short
+    // enough to balance against the rest, and not so many that their merge
+    // and per-item round trips dominate).
+    const int64_t parts0 = ((int64_t)max_context_len + p - 1) / p;
+    if (parts0 > 1 && (int64_t)num_seqs * parts0 * num_kv_heads > kGridLimit) p = kWorkListPartition;
+  }
   int32_t head_fastest = 0;
   int merge_mode = -1;  // -1: chosen below
 #ifdef MVK_TUNING
