@@ -22,9 +22,6 @@ constexpr int32_t kMaxGridYZ = 65535;
 // grid would be partitions past short contexts, each costing a dispatch and a
 // load only to exit.
 constexpr int64_t kGridLimit = 16384;
-// Partition length (tokens) the library chooses for batches that run in
-// work-list mode.
-constexpr int32_t kWorkListPartition = 3072;
 // Shortest longest-context (tokens) for which a single-pass grid is
 // dispatched longest sequence first.
 constexpr int32_t kMinOrderedContext = 1024;
@@ -63,9 +60,15 @@ int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_co
   return cap < 256 ? cap : 256;
 }
 
+// Partition length (tokens) the library chooses for batches that run in
+// work-list mode.
+constexpr int32_t kWorkListPartition = 3072;
+
 // Waves per workgroup: 8 for the longest partitions (more bytes in flight per
 // workgroup), else 4.
-int32_t default_waves(int32_t partition_tokens) { return partition_tokens >= 4096 ? 8 : 4; }
+int32_t default_waves(int32_t partition_tokens) {
+  return partition_tokens >= kWorkListPartition ? 8 : 4;
+}
 
 struct Plan {
   int32_t partition_tokens;
@@ -93,7 +96,6 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   if (!mvk::decode_supported(head_dim, num_q_heads / num_kv_heads)) return MVK_ERR_UNSUPPORTED;
   int32_t p = partition_tokens ? partition_tokens
                                : default_partition(num_seqs, num_kv_heads, max_context_len);
-  int32_t waves = default_waves(p);
   if (!partition_tokens && p == kMaxPartition) {
     // A batch whose dense grid at the longest partitions would run in
     // work-list mode (a few very long sequences among many short ones) takes
@@ -105,6 +107,9 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     const int64_t parts0 = ((int64_t)max_context_len + p - 1) / p;
     if (parts0 > 1 && (int64_t)num_seqs * parts0 * num_kv_heads > kGridLimit) p = kWorkListPartition;
   }
+  // a function of the partition length alone, so that a caller passing the
+  // length the library chose gets the same plan
+  int32_t waves = default_waves(p);
   int32_t head_fastest = 0;
   int merge_mode = -1;  // -1: chosen below
 #ifdef MVK_TUNING
