@@ -147,6 +147,20 @@ def test_workspace_size(mvk):
         mvk.workspace_size(2, 3, 2, 64, 10)
 
 
+def test_library_partition_choice(mvk):
+    """The partition lengths the planner picks for the benchmark's shapes: a
+    single pass for short and medium contexts, 4096 tokens for a dense grid
+    of long contexts, 3072 for a batch that runs in work-list mode (a few
+    very long sequences among many short ones)."""
+    assert mvk.workspace_size(60, 16, 8, 128, 256) == (0, 256)          # Qwen3 shape
+    assert mvk.workspace_size(256, 32, 4, 64, 2048) == (0, 2048)        # TinyLlama shape
+    assert mvk.workspace_size(32, 32, 8, 128, 32768)[1] == 4096         # Llama-7B long
+    nbytes, p = mvk.workspace_size(512, 16, 8, 128, 131072)             # skewed batch
+    parts = -(-131072 // 3072)
+    assert p == 3072
+    assert nbytes == 65536 + 512 * 16 * parts * 130 * 4 + (1 + 8 + 2 * 512 * parts) * 4
+
+
 def mq_call(mvk, **over):
     a = dict(out=FAKE, q=FAKE * 2, k=FAKE * 3, v=FAKE * 4, bt=FAKE * 5, cl=FAKE * 6, qs=FAKE * 7,
              S=4, T=12, mq=5, hq=4, hkv=2, d=64, bs=16, nb=32, mb=4, maxlen=45, scale=0.125,
