@@ -31,13 +31,19 @@ __device__ __forceinline__ int sequence_of_rank(const int32_t* __restrict__ cont
   const int idx_bits = 32 - __builtin_clz((unsigned)max(S - 1, 1));
   const int max_blocks = (max_context_len + kBlockTokens - 1) / kBlockTokens;
   const int blk_bits = 32 - __builtin_clz((unsigned)max(max_blocks, 1));
+  const int nk = (S + 63) / 64;  // key slots in use (uniform)
+  // Every lane loads all its lengths at once (indexes clamped into the batch,
+  // so no load is conditional and one wait covers them all).
+  int Lraw[kOrderKeys];
+#pragma unroll
+  for (int k = 0; k < kOrderKeys; ++k) Lraw[k] = context_lens[min(lane + 64 * k, S - 1)];
   uint32_t key[kOrderKeys];
   bool valid[kOrderKeys];
 #pragma unroll
   for (int k = 0; k < kOrderKeys; ++k) {
     const int s = lane + 64 * k;
     valid[k] = s < S;
-    const int L = valid[k] ? min(max(context_lens[s], 0), max_context_len) : 0;
+    const int L = valid[k] ? min(max(Lraw[k], 0), max_context_len) : 0;
     key[k] = ((uint32_t)((L + kBlockTokens - 1) / kBlockTokens) << idx_bits) |
              (uint32_t)(valid[k] ? S - 1 - s : 0);
   }
@@ -48,7 +54,7 @@ __device__ __forceinline__ int sequence_of_rank(const int32_t* __restrict__ cont
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < kOrderKeys; ++k) {
-      cnt += __builtin_popcountll(__ballot(valid[k] && (key[k] >> b) == want));
+      if (k < nk) cnt += __builtin_popcountll(__ballot(valid[k] && (key[k] >> b) == want));
     }
     if (rem < cnt) prefix |= 1u << b;
     else rem -= cnt;
