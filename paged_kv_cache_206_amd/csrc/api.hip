@@ -76,6 +76,7 @@ struct Plan {
   int32_t waves;
   int32_t head_fastest;
   int32_t longest_first;
+  int32_t detect_shared;
   bool work_list;
   int32_t list_workgroups;
   size_t counter_bytes;    // the counter region at the start of the workspace
@@ -137,6 +138,13 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   // (about 1.5 us) is repaid: dispatch longest first. Measured on MI355X:
   // 256 x 4 items of 512-2048 tokens 71.5 -> 68.6 us; 60 x 8 items of
   // 64-256 tokens 11.2 -> 12.1 us (so short contexts keep batch order).
+  // Dense grids of split sequences (long contexts, where a shared prefix is
+  // many blocks) look for blocks shared with a neighbouring sequence and
+  // keep those cached; the lookup costs more than it saves on short contexts
+  // and on work lists (measured with it on everywhere: Llama-7B shape 534.6
+  // -> 526 us, the Qwen3 shape 11.24 -> 11.89 us, the skewed batch 351 ->
+  // 363 us).
+  plan->detect_shared = parts > 1 && !plan->work_list;
   plan->longest_first = parts == 1 && num_seqs <= mvk::kMaxOrderedSeqs &&
                         max_context_len >= kMinOrderedContext && !head_fastest;
   if (!plan->work_list && dense > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
@@ -172,6 +180,7 @@ struct MqPlan {
   int32_t tiles;           // 16-row tiles per workgroup
   int32_t row_groups;      // workgroups per (sequence, KV head, partition)
   int32_t longest_first;   // as in decode: single pass, <= 256 sequences, long contexts
+  int32_t detect_shared;   // as in decode: sequences split into several partitions
   size_t workspace_bytes;  // partial (m, l, o) states, when sequences are split
 };
 
@@ -223,6 +232,7 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
   // Row groups of one (sequence, KV head) read the same blocks: in the
   // XCD-contiguous order they share an L2, in longest-first order they would
   // not, so several row groups keep that order.
+  plan->detect_shared = parts > 1;
   plan->longest_first = parts == 1 && row_groups == 1 && num_seqs <= mvk::kMaxOrderedSeqs &&
                         max_context_len >= kMinOrderedContext;
   plan->workspace_bytes = parts > 1 ? (size_t)num_query_tokens * num_q_heads * (size_t)parts *
@@ -277,7 +287,7 @@ int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads
                                            size_t* workspace_bytes,
                                            int32_t* chosen_partition_tokens) {
   if (!workspace_bytes) return MVK_ERR_INVALID_ARGUMENT;
-  Plan plan;
+  Plan plan{};
   const int32_t st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                  partition_tokens, &plan);
   if (st != MVK_OK) return st;
@@ -301,7 +311,7 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
     return MVK_ERR_INVALID_ARGUMENT;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
     return MVK_ERR_INVALID_ARGUMENT;
-  Plan plan;
+  Plan plan{};
   const int32_t st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                  partition_tokens, &plan);
   if (st != MVK_OK) return st;
@@ -324,7 +334,7 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
     if (!aligned16(workspace)) return MVK_ERR_INVALID_ARGUMENT;
   }
 
-  mvk::DecodeArgs a;
+  mvk::DecodeArgs a{};
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
@@ -353,6 +363,7 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
   a.waves = plan.waves;
   a.head_fastest = plan.head_fastest;
   a.longest_first = plan.longest_first;
+  a.detect_shared = plan.detect_shared;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;
   hipError_t err = mvk::launch_paged_decode(a, (hipStream_t)stream);
@@ -364,7 +375,7 @@ int32_t mvk_paged_attention_multi_query_workspace_size(
     int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len, int32_t partition_tokens,
     size_t* workspace_bytes, int32_t* chosen_partition_tokens) {
   if (!workspace_bytes) return MVK_ERR_INVALID_ARGUMENT;
-  MqPlan plan;
+  MqPlan plan{};
   const int32_t st = check_mq_sizes(num_seqs, num_query_tokens, max_query_len, num_q_heads,
                                     num_kv_heads, head_dim, max_context_len, partition_tokens,
                                     &plan);
@@ -387,7 +398,7 @@ int32_t mvk_paged_attention_multi_query(
     return MVK_ERR_INVALID_ARGUMENT;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
     return MVK_ERR_INVALID_ARGUMENT;
-  MqPlan plan;
+  MqPlan plan{};
   const int32_t st = check_mq_sizes(num_seqs, num_query_tokens, max_query_len, num_q_heads,
                                     num_kv_heads, head_dim, max_context_len, partition_tokens,
                                     &plan);
@@ -405,7 +416,7 @@ int32_t mvk_paged_attention_multi_query(
     if (!aligned16(workspace)) return MVK_ERR_INVALID_ARGUMENT;
   }
 
-  mvk::MultiQueryArgs a;
+  mvk::MultiQueryArgs a{};
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
@@ -430,6 +441,7 @@ int32_t mvk_paged_attention_multi_query(
   a.tiles = plan.tiles;
   a.row_groups = plan.row_groups;
   a.longest_first = plan.longest_first;
+  a.detect_shared = plan.detect_shared;
   a.waves = plan.waves;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;

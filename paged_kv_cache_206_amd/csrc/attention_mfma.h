@@ -109,16 +109,17 @@ struct MfmaPolicy {
 
   // kr/vr: this KV head's slice of one block (a scalar descriptor; every lane
   // adds its fixed offset); rows past the context read as 0
+  template <int POL>
   __device__ __forceinline__ void load(Frag& f, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                        uint32_t row_bytes) const {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      f.k[ks] = buffer_load16<kStreamLoad>(kr, koff + 128u * (ks >> 1) + 8u * (ks & 1) * row_bytes);
+      f.k[ks] = buffer_load16<POL>(kr, koff + 128u * (ks >> 1) + 8u * (ks & 1) * row_bytes);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (D == 128) f.v[i] = buffer_load16<kStreamLoad>(vr, voff + i * row_bytes);
-      else f.v[i] = buffer_load8<kStreamLoad>(vr, voff + i * row_bytes);
+      if constexpr (D == 128) f.v[i] = buffer_load16<POL>(vr, voff + i * row_bytes);
+      else f.v[i] = buffer_load8<POL>(vr, voff + i * row_bytes);
     }
   }
 

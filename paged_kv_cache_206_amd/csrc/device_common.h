@@ -93,6 +93,19 @@ __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, POLICY));
 }
 
+// Blocks a sequence shares with a neighbour in the batch. Lane k holds
+// entry k of a wave's block list (ent) and the entries at the same logical
+// positions of the previous and next sequences' tables (-1 where there is
+// none); bit k of the result is set when block k is also one of theirs.
+// Sequences that share a prefix (a common prompt, parallel samples) sit next
+// to each other in a batch, and their shared blocks are read by several
+// workgroups at about the same time: those loads keep the default cache
+// policy, so the blocks stay in L2 for the other readers, while every other
+// block streams (kStreamLoad). A false match only changes a cache policy.
+__device__ __forceinline__ uint64_t shared_blocks(int ent, int ent_prev, int ent_next) {
+  return __ballot(ent == ent_prev || ent == ent_next);
+}
+
 // Device-coherent float store / load (relaxed atomics at device scope): they
 // bypass the per-XCD L2's non-coherent state, so a value published by one
 // workgroup is seen by a workgroup on another XCD without any cache-wide

@@ -34,6 +34,7 @@ struct DecodeArgs {
   int32_t waves;     // waves per workgroup (4 or 8)
   int32_t head_fastest;  // grid order (see Shape)
   int32_t longest_first; // single-pass grid dispatched longest sequence first (see Shape)
+  int32_t detect_shared; // blocks shared with a neighbouring sequence keep the default cache policy
   int32_t* items;    // work list (count, one dispatch counter per KV head, then (seq, part)
                      // pairs); nullptr = grid mode
   int32_t* counters; // per (seq, KV head) partition counters (zero between calls), or
@@ -65,6 +66,7 @@ struct MultiQueryArgs {
   int32_t row_groups;  // groups of 16 * tiles (new token, query head) rows per (sequence, KV head)
   int32_t waves;       // waves per workgroup (4 or 8)
   int32_t longest_first;  // single-pass grid dispatched longest sequence first
+  int32_t detect_shared;  // blocks shared with a neighbouring sequence keep the default cache policy
   float scale_log2;
   int32_t dtype;
 };

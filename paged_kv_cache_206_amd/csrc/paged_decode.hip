@@ -54,6 +54,7 @@ namespace mvk {
 constexpr int kPrefetch = 2;
 
 struct Shape {
+  int32_t num_seqs;
   int32_t num_kv_heads, num_blocks, max_blocks, max_context_len, partition_tokens, num_parts;
   float scale_log2;
   int32_t head_fastest;  // grid order: 1 = (KV head, sequence, partition), 0 = (sequence, KV head, partition)
@@ -101,13 +102,14 @@ struct ValuPolicy {
     }
   }
 
+  template <int POL>
   __device__ __forceinline__ void load(Frag& f, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                        uint32_t row_bytes) const {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       const uint32_t o = off + i * RG * row_bytes;
-      f.k[i] = buffer_load16<kStreamLoad>(kr, o);
-      f.v[i] = buffer_load16<kStreamLoad>(vr, o);
+      f.k[i] = buffer_load16<POL>(kr, o);
+      f.v[i] = buffer_load16<POL>(vr, o);
     }
   }
 
@@ -201,7 +203,7 @@ struct ValuPolicy {
 // [part*P, min((part+1)*P, L))): the final row if the context fits in one
 // partition, else this partition's partial state. Every wave of the workgroup
 // calls it with the same arguments (it contains a barrier).
-template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED>
+template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED, bool SHARED>
 __device__ __forceinline__ void decode_item(
     int s, int h, int part, uint16_t* __restrict__ out, float* __restrict__ ws_ml,
     float* __restrict__ ws_o, const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
@@ -228,8 +230,15 @@ __device__ __forceinline__ void decode_item(
   if constexpr (FUSED) slot = slots[s];
   const int part_blocks = min(P / kBlockTokens, sh.max_blocks - b_begin);
   const int32_t* table = block_tables + (size_t)s * sh.max_blocks;
-  int ent = 0;
-  if (wave + lane * W < part_blocks) ent = table[b_begin + wave + lane * W];
+  int ent = 0, ent_prev = -1, ent_next = -1;
+  if (wave + lane * W < part_blocks) {
+    const int e = b_begin + wave + lane * W;
+    ent = table[e];
+    if constexpr (SHARED) {  // the same logical blocks of the neighbouring sequences
+      if (s > 0) ent_prev = table[e - sh.max_blocks];
+      if (s + 1 < sh.num_seqs) ent_next = table[e + sh.max_blocks];
+    }
+  }
   const int Hq = sh.num_kv_heads * G;
   const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;  // one token row of the pool
   const size_t new_src = ((size_t)s * sh.num_kv_heads + h) * D;
@@ -294,6 +303,8 @@ __device__ __forceinline__ void decode_item(
     int blk = __builtin_amdgcn_readlane(ent, min(k, my_blocks - 1));
     return ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
   };
+  uint64_t shared = 0;
+  if constexpr (SHARED) shared = shared_blocks(ent, ent_prev, ent_next);
   auto load_block = [&](typename Policy::Frag& fr, int k) {
     const bool real = k < my_blocks;
     const int blk = block_of(k);
@@ -301,7 +312,9 @@ __device__ __forceinline__ void decode_item(
     const int rows = min(kBlockTokens, t_end - tok_of(k));
     const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
     const size_t o = (size_t)blk * block_bytes;
-    pol.load(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + o, extent), vr = make_rsrc(vbase + o, extent);
+    if (SHARED && ((shared >> k) & 1u)) pol.template load<kDefaultLoad>(fr, kr, vr, row_bytes);
+    else pol.template load<kStreamLoad>(fr, kr, vr, row_bytes);
   };
   auto is_new = [&](int k) { return FUSED && block_of(k) == blk_new; };
   if (my_blocks > 0) {
@@ -417,7 +430,7 @@ __device__ __forceinline__ void decode_item(
 template <int D, int G>
 constexpr int kMinWavesPerSimd = (D == 64 || G == 1) ? 4 : 2;
 
-template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED>
+template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED, bool SHARED>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<D, G>))) void paged_decode_partition_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
@@ -451,7 +464,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMinWave
       h = sh.head_fastest ? v % H : (v / S) % H;
       part = v / (S * H);
     }
-    decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
+    decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED, SHARED>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
                                                block_tables, context_lens, sh, new_key,
                                                new_value, slots, counters, sm_o, sm_m, sm_l,
                                                &sm_last, sm_new[0], sm_new[1]);
@@ -469,7 +482,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMinWave
     if (i >= count) break;  // uniform over the workgroup
     const int s = pairs[2 * i];
     const int part = pairs[2 * i + 1];
-    decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache,
+    decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED, SHARED>(s, blockIdx.y, part, out, ws_ml, ws_o, q, k_cache,
                                                v_cache, block_tables, context_lens, sh, new_key,
                                                new_value, slots, counters, sm_o, sm_m, sm_l,
                                                &sm_last, sm_new[0], sm_new[1]);
@@ -614,9 +627,9 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_kernel(
   }
 }
 
-template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED>
+template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED, bool SHARED>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  Shape sh{a.num_kv_heads, a.num_blocks, a.max_blocks_per_seq, a.max_context_len,
+  Shape sh{a.num_seqs, a.num_kv_heads, a.num_blocks, a.max_blocks_per_seq, a.max_context_len,
            a.partition_tokens, a.num_parts, a.scale_log2, a.head_fastest, a.longest_first};
   dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_parts);
   if (a.items != nullptr) {
@@ -627,7 +640,7 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     grid = dim3((unsigned)a.list_workgroups, (unsigned)a.num_kv_heads, 1u);
   }
-  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, W, NPF, USE_MFMA, FUSED>), grid,
+  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, W, NPF, USE_MFMA, FUSED, SHARED>), grid,
                      dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
                      (const uint16_t*)a.q, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache,
                      a.block_tables, a.context_lens, a.items, sh,
@@ -642,6 +655,20 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Blocks shared with a neighbouring sequence are looked for (and kept
+// cached) only in the kernels of split long-context grids: the choice
+// between two load variants costs the other shapes 4-7 % even when nothing
+// is shared, so it is a separate instantiation.
+template <int DT, int D, int G, int W, bool MFMA>
+static hipError_t launch_shared(const DecodeArgs& a, bool fused, hipStream_t stream) {
+  if (a.detect_shared) {
+    return fused ? launch_typed<DT, D, G, W, kPrefetch, MFMA, true, true>(a, stream)
+                 : launch_typed<DT, D, G, W, kPrefetch, MFMA, false, true>(a, stream);
+  }
+  return fused ? launch_typed<DT, D, G, W, kPrefetch, MFMA, true, false>(a, stream)
+               : launch_typed<DT, D, G, W, kPrefetch, MFMA, false, false>(a, stream);
+}
+
 template <int DT, int D, int G>
 static hipError_t launch_waves(const DecodeArgs& a, hipStream_t stream) {
   // MFMA from g = 2 on: at g = 2 it takes the Qwen3-shaped call (60 x 8 short
@@ -650,10 +677,8 @@ static hipError_t launch_waves(const DecodeArgs& a, hipStream_t stream) {
   constexpr bool kMfma = G >= 2;
   const bool fused = a.new_key != nullptr;
   switch (a.waves) {
-    case 4: return fused ? launch_typed<DT, D, G, 4, kPrefetch, kMfma, true>(a, stream)
-                         : launch_typed<DT, D, G, 4, kPrefetch, kMfma, false>(a, stream);
-    case 8: return fused ? launch_typed<DT, D, G, 8, kPrefetch, kMfma, true>(a, stream)
-                         : launch_typed<DT, D, G, 8, kPrefetch, kMfma, false>(a, stream);
+    case 4: return launch_shared<DT, D, G, 4, kMfma>(a, fused, stream);
+    case 8: return launch_shared<DT, D, G, 8, kMfma>(a, fused, stream);
     default: return hipErrorInvalidValue;
   }
 }

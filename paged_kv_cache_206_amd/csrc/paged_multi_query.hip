@@ -84,7 +84,7 @@ __device__ __forceinline__ size_t mq_out_row(int first_token, int r, int h, int 
 template <int D, int NT>
 constexpr int kMqMinWavesPerSimd = (D == 64 && NT == 1) ? 4 : 2;
 
-template <int DT, int D, int G, int W, int NT>
+template <int DT, int D, int G, int W, int NT, bool SHARED>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMqMinWavesPerSimd<D, NT>)))
 void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                                float* __restrict__ ws_o, const uint16_t* __restrict__ q,
@@ -127,8 +127,15 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
   const int qs1 = query_start[s + 1];
   const int part_blocks = min(P / kBlockTokens, sh.max_blocks - b_begin);
   const int32_t* table = block_tables + (size_t)s * sh.max_blocks;
-  int ent = 0;
-  if (wave + lane * W < part_blocks) ent = table[b_begin + wave + lane * W];
+  int ent = 0, ent_prev = -1, ent_next = -1;
+  if (wave + lane * W < part_blocks) {
+    const int e = b_begin + wave + lane * W;
+    ent = table[e];
+    if constexpr (SHARED) {  // the same logical blocks of the neighbouring sequences
+      if (s > 0) ent_prev = table[e - sh.max_blocks];
+      if (s + 1 < sh.num_seqs) ent_next = table[e + sh.max_blocks];
+    }
+  }
 
   const int L = min(len, sh.max_context_len);
   int first, n_new;
@@ -170,6 +177,8 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
     // (rows past the context read as zeros), steps past the last block
     // issuing loads through an empty descriptor.
     typename Policy::Frag f[NPF];
+    uint64_t shared = 0;
+    if constexpr (SHARED) shared = shared_blocks(ent, ent_prev, ent_next);
     auto tok_of = [&](int k) { return (b_begin + wave + k * W) * kBlockTokens; };
     auto load_block = [&](typename Policy::Frag& fr, int k) {
       const bool real = k < my_blocks;
@@ -179,7 +188,9 @@ void paged_mq_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ w
       const int nrows = min(kBlockTokens, t_end - tok_of(k));
       const uint32_t extent = real ? (uint32_t)(nrows - 1) * row_bytes + D * 2u : 0u;
       const size_t o = (size_t)blk * block_bytes;
-      pol[0].load(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent), row_bytes);
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + o, extent), vr = make_rsrc(vbase + o, extent);
+      if (SHARED && ((shared >> k) & 1u)) pol[0].template load<kDefaultLoad>(fr, kr, vr, row_bytes);
+      else pol[0].template load<kStreamLoad>(fr, kr, vr, row_bytes);
     };
 #pragma unroll
     for (int j = 0; j < NPF - 1; ++j) load_block(f[j], j);
@@ -282,13 +293,13 @@ __global__ __launch_bounds__(kMqMergeThreads) void paged_mq_merge_kernel(
   }
 }
 
-template <int DT, int D, int G, int W, int NT>
+template <int DT, int D, int G, int W, int NT, bool SHARED>
 hipError_t launch_mq_typed(const MultiQueryArgs& a, hipStream_t stream) {
   MqShape sh{a.num_seqs,       a.num_kv_heads,  a.num_blocks,       a.max_blocks_per_seq,
              a.max_context_len, a.max_query_len, a.partition_tokens, a.num_parts,
              a.row_groups,      a.num_query_tokens, a.scale_log2, a.longest_first};
   const int64_t items = (int64_t)a.row_groups * a.num_seqs * a.num_kv_heads * a.num_parts;
-  hipLaunchKernelGGL((paged_mq_partition_kernel<DT, D, G, W, NT>), dim3((unsigned)items),
+  hipLaunchKernelGGL((paged_mq_partition_kernel<DT, D, G, W, NT, SHARED>), dim3((unsigned)items),
                      dim3(W * 64), 0, stream, (uint16_t*)a.out, a.ws_ml, a.ws_o,
                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                      (const uint16_t*)a.v_cache, a.block_tables, a.context_lens, a.query_start,
@@ -306,8 +317,10 @@ hipError_t launch_mq_typed(const MultiQueryArgs& a, hipStream_t stream) {
 template <int DT, int D, int G, int NT>
 hipError_t launch_mq_waves(const MultiQueryArgs& a, hipStream_t stream) {
   switch (a.waves) {
-    case 4: return launch_mq_typed<DT, D, G, 4, NT>(a, stream);
-    case 8: return launch_mq_typed<DT, D, G, 8, NT>(a, stream);
+    case 4: return a.detect_shared ? launch_mq_typed<DT, D, G, 4, NT, true>(a, stream)
+                                   : launch_mq_typed<DT, D, G, 4, NT, false>(a, stream);
+    case 8: return a.detect_shared ? launch_mq_typed<DT, D, G, 8, NT, true>(a, stream)
+                                   : launch_mq_typed<DT, D, G, 8, NT, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

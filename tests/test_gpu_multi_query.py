@@ -203,3 +203,33 @@ def test_longest_first_order_writes_every_row(num_seqs, dtype, d, g):
     ref, _ = oracle_mq(wl, q, qs)
     err = max_err(out, ref, wl.dtype)
     assert err <= TOL[wl.dtype], f"max abs err {err:.3e} > {TOL[wl.dtype]}"
+
+
+def test_shared_prefix_equals_copied_blocks_bitwise():
+    """Sequences whose tables share their first blocks (a common prompt): the
+    split kernels keep blocks shared with a neighbouring sequence cached
+    instead of streaming them, which must change nothing in the result - the
+    same call over private copies of those blocks gives the same bits."""
+    lens, news = [600, 700, 517, 33], [3, 1, 4, 2]
+    shared = W.make_custom("s", "bf16", lens, 8, 2, 128, 200, seed=9,
+                           shared_prefix=({0, 1, 2, 3}, 2))
+    q, qs = W.make_queries(shared, news, 10)
+    layer = shared.layers[0]
+    bt = shared.block_tables.clone()
+    k, v = layer.k_cache.clone(), layer.v_cache.clone()
+    used = set(int(x) for x in shared.used_block_ids())
+    free = [b for b in range(shared.num_blocks) if b not in used]
+    for s in range(1, 4):
+        for b in range(2):
+            src = int(bt[s, b])
+            dst = free.pop()
+            k[dst], v[dst] = k[src], v[src]
+            bt[s, b] = dst
+    copied = W.Workload("c", "bf16", 4, 8, 2, 128, shared.num_blocks, shared.scale,
+                        shared.context_lens, bt, [W.Layer(layer.q, k, v)])
+    for p in (0, 128):
+        a = gpu_mq(shared.to("cuda"), q.to("cuda"), qs.to("cuda"), partition_tokens=p)
+        b = gpu_mq(copied.to("cuda"), q.to("cuda"), qs.to("cuda"), partition_tokens=p)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    parity(shared, q, qs, partition_tokens=128)
