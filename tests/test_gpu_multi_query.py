@@ -160,6 +160,26 @@ def test_speculative_verification_qwen3_shape():
     parity(wl, q, qs)
 
 
+def test_speculative_verification_tinyllama_shape_sampled():
+    """The TinyLlama-1.1B decode shape (256 x 512-2048 tokens, g = 8) with 2
+    draft tokens (3 new tokens per sequence), full size and in the launch
+    configuration the benchmark times (single pass, dispatched longest
+    first); 32 sequences checked against the oracle."""
+    wl = W.make("tinyllama")
+    q, qs = W.make_queries(wl, [3] * wl.num_seqs, seed=78)
+    parity(wl, q, qs, seqs=list(range(0, 256, 8)))
+
+
+def test_speculative_verification_llama7b_long_sampled():
+    """The Llama-7B long-context shape (32 x 32768 tokens, 16 sequences sharing
+    a 16384-token prefix) with 4 draft tokens, full size, in the benchmark's
+    launch configuration (split, shared prefix blocks kept cached); two
+    prefix sharers and two private sequences checked."""
+    wl = W.make("llama7b_long")
+    q, qs = W.make_queries(wl, [5] * wl.num_seqs, seed=79)
+    parity(wl, q, qs, seqs=[0, 15, 16, 31])
+
+
 def test_long_context_verification_sampled():
     """Long contexts (8 x 16384 tokens, 5 new each) through the split path;
     4 sequences are checked against the oracle."""
