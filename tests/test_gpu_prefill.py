@@ -159,3 +159,30 @@ def test_long_prompt_llama_shape_sampled_rows():
                     for r in rows])
     err = max_err(out[torch.as_tensor(rows, device="cuda")], ref, "bf16")
     assert err <= TOL["bf16"]
+
+
+def test_llama_shape_full_batch_sampled_rows():
+    """The benchmark's Llama-7B prefill call at full size (32 prompts x 4096
+    tokens, 32 q / 8 kv heads, head_dim 128, bf16, fused cache write, the
+    library's launch configuration): rows at tile and range boundaries of the
+    first, a middle and the last prompt, each against a single-row oracle call
+    over the oracle's own cache write; the whole pools bit-exact."""
+    S, n = 32, 4096
+    pf = W.make_prefill("bf16", [n] * S, 32, 8, 128, seed=11)
+    g = pf.to("cuda")
+    out = gpu_prefill(g)
+    torch.cuda.synchronize()
+    q = bits(pf.q)
+    kc, vc = oracle.cache_write(bits(pf.k_cache), bits(pf.v_cache), bits(pf.key), bits(pf.value),
+                                pf.slot_mapping.numpy())
+    assert np.array_equal(bits(g.k_cache), kc) and np.array_equal(bits(g.v_cache), vc)
+    bt = pf.block_tables.numpy()
+    cu = pf.cu_seqlens.numpy()
+    picks = [(p, r) for p in (0, 17, S - 1) for r in (0, 15, 16, 127, 128, 2047, 2048, 4095)]
+    ref = np.stack([oracle.paged_multi_query(q[cu[p] + r:cu[p] + r + 1], kc, vc, bt[p:p + 1],
+                                             np.array([r + 1], dtype=np.int32),
+                                             np.array([0, 1], dtype=np.int32), pf.scale, "bf16")[0]
+                    for p, r in picks])
+    rows = torch.as_tensor([int(cu[p]) + r for p, r in picks], device="cuda")
+    err = max_err(out[rows], ref, "bf16")
+    assert err <= TOL["bf16"], f"max abs err {err:.3e}"
