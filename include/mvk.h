@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MVK_ABI_VERSION 5
+#define MVK_ABI_VERSION 6
 
 typedef enum mvk_status {
     MVK_OK = 0,
@@ -122,6 +122,19 @@ int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads
                                            int32_t max_context_len, int32_t partition_tokens,
                                            size_t* workspace_bytes,
                                            int32_t* chosen_partition_tokens);
+
+/*
+ * mvk_paged_attention_workspace_bytes - workspace bytes that suffice for
+ * mvk_paged_attention_decode with these sizes and the library's choice of
+ * partition length (partition_tokens = 0), whatever the number of KV heads:
+ * the largest of mvk_paged_attention_workspace_size's answers over every
+ * supported group size num_q_heads / num_kv_heads (1, 2, 4, 8). A caller that
+ * knows num_kv_heads gets the exact size from mvk_paged_attention_workspace_size.
+ * Returns SIZE_MAX when no group size gives valid sizes (e.g. head_dim not 64
+ * or 128, negative sizes).
+ */
+size_t mvk_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t head_dim, int32_t max_context_len);
 
 /*
  * mvk_paged_attention_decode - one batched decode step of paged attention,
@@ -287,10 +300,15 @@ int32_t mvk_paged_attention_multi_query(void* out, const void* q,
  *                 Offsets outside [0, num_tokens] are clamped into it (no
  *                 access outside the token arrays; rows of a prompt longer
  *                 than the grid covers are not computed).
+ *   scale         finite and > 0 (MVK_ERR_UNSUPPORTED otherwise: the kernel takes
+ *                 the running maximum of the raw dot products and scales it).
  *   head_dim 64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
  *   block_size 16. num_seqs == 0 or num_tokens == 0 is a no-op.
  *   A prompt's rows are addressed with 32-bit byte offsets: (max_seqlen + 256)
  *   * num_kv_heads * head_dim * 2 above INT32_MAX is MVK_ERR_UNSUPPORTED.
+ *   Inputs are finite numbers: the kernel is compiled without NaN semantics,
+ *   so a NaN in q, key or value gives an unspecified output (it is not
+ *   guaranteed to propagate).
  * Repeated calls give identical bits.
  * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED, MVK_ERR_HIP.
  */
@@ -300,6 +318,20 @@ int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const v
                               int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
                               float scale, int32_t dtype, void* stream);
+
+/*
+ * mvk_stream_read_probe - measurement aid: a read-only streaming kernel over
+ * `bytes` bytes of device memory at `src`, with the same 16-byte loads and
+ * non-temporal cache policy as the attention kernels' K/V streams, giving the
+ * practical HBM read rate that their byte rates are compared with. Workgroup
+ * i of `workgroups` (256 threads each) writes one uint32 to sink[i] so that no
+ * load is dead; nothing else is written.
+ *   src   device, 16-byte aligned; bytes a multiple of 16 in [16, 2^31].
+ *   sink  device uint32 [workgroups]; workgroups in [1, 65535].
+ * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_HIP.
+ */
+int32_t mvk_stream_read_probe(const void* src, size_t bytes, void* sink, int32_t workgroups,
+                              void* stream);
 
 /*
  * Block manager (host side): which physical 16-token blocks each sequence

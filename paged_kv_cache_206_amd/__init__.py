@@ -9,6 +9,7 @@ is no fallback: if libmvk.so is missing, the first call fails with instructions.
                            max_context_len=None, out=None, partition_tokens=0,
                            workspace=None, new_key=None, new_value=None,
                            slot_mapping=None)
+    workspace_size(...), workspace_bytes(...)
     paged_attention_multi_query(q, k_cache, v_cache, block_tables, context_lens,
                                 query_start, scale, max_query_len=None,
                                 max_context_len=None, out=None, partition_tokens=0,
@@ -31,7 +32,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmvk.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 MVK_OK = 0
 MVK_ERR_INVALID_ARGUMENT = 1
 MVK_ERR_UNSUPPORTED = 2
@@ -53,10 +54,12 @@ SIGNATURES = {
     "mvk_paged_attention_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                                     ctypes.POINTER(_c_size),
                                                     ctypes.POINTER(_c_int)]),
+    "mvk_paged_attention_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "mvk_paged_attention_decode": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int, _c_int, _c_float, _c_int, _c_int, _ptr,
                                             _c_size, _ptr]),
+    "mvk_stream_read_probe": (_c_int, [_ptr, _c_size, _ptr, _c_int, _ptr]),
     "mvk_paged_attention_multi_query_workspace_size": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                  ctypes.POINTER(_c_size), ctypes.POINTER(_c_int)]),
@@ -195,25 +198,20 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
     return nbytes.value, chosen.value
 
 
-def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                           max_context_len: int | None = None, out: torch.Tensor | None = None,
-                           partition_tokens: int = 0, workspace: torch.Tensor | None = None,
-                           new_key: torch.Tensor | None = None,
-                           new_value: torch.Tensor | None = None,
-                           slot_mapping: torch.Tensor | None = None) -> torch.Tensor:
-    """One batched decode step: out[s, j] = softmax(scale * q[s, j] K_s^T) V_s
-    over the context_lens[s] tokens reached through block_tables[s].
+def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int) -> int:
+    """Workspace bytes that suffice for the decode call at these sizes with the
+    library's partition choice, for any number of KV heads (an upper bound;
+    workspace_size() gives the exact figure). Raises on invalid sizes."""
+    n = lib().mvk_paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise MvkError("mvk_paged_attention_workspace_bytes", MVK_ERR_INVALID_ARGUMENT)
+    return n
 
-    With new_key / new_value ([S, Hkv, D]) and slot_mapping (int32 [S]) the
-    step's cache write is fused in: row s is stored at slot_mapping[s] and
-    sequence s attends over it.
 
-    `max_context_len` must bound context_lens; when omitted it is read from the
-    device (a synchronising copy). `workspace` (uint8, on the device, at least
-    workspace_size() bytes) must be zero-filled before its first use; calls
-    leave it ready for the next call. It is allocated through torch when
-    needed and not given."""
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
+                 new_key, new_value, slot_mapping):
+    """Checks shared by the two decode entry points; returns the pieces of the
+    C call that do not depend on the workspace."""
     _require(q, "q", ndim=3)
     _require(k_cache, "k_cache", dtype=q.dtype, ndim=4)
     _require(v_cache, "v_cache", dtype=q.dtype, ndim=4)
@@ -245,6 +243,31 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _require(out, "out", dtype=q.dtype)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
+    return S, hq, hkv, d, nb, bs, nk, nv, sm, max_context_len, out
+
+
+def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                           max_context_len: int | None = None, out: torch.Tensor | None = None,
+                           partition_tokens: int = 0, workspace: torch.Tensor | None = None,
+                           new_key: torch.Tensor | None = None,
+                           new_value: torch.Tensor | None = None,
+                           slot_mapping: torch.Tensor | None = None) -> torch.Tensor:
+    """One batched decode step: out[s, j] = softmax(scale * q[s, j] K_s^T) V_s
+    over the context_lens[s] tokens reached through block_tables[s].
+
+    With new_key / new_value ([S, Hkv, D]) and slot_mapping (int32 [S]) the
+    step's cache write is fused in: row s is stored at slot_mapping[s] and
+    sequence s attends over it.
+
+    `max_context_len` must bound context_lens; when omitted it is read from the
+    device (a synchronising copy). `workspace` (uint8, on the device, at least
+    workspace_size() bytes) must be zero-filled before its first use; calls
+    leave it ready for the next call. It is allocated through torch when
+    needed and not given."""
+    S, hq, hkv, d, nb, bs, nk, nv, sm, max_context_len, out = _decode_args(
+        q, k_cache, v_cache, block_tables, context_lens, max_context_len, out, new_key,
+        new_value, slot_mapping)
     need, _ = workspace_size(S, hq, hkv, d, max_context_len, partition_tokens)
     ws_ptr, ws_bytes = None, 0
     if need:
@@ -263,6 +286,18 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                                   workspace))
     _check("mvk_paged_attention_decode", st)
     return out
+
+
+def stream_read_probe(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None) -> None:
+    """Measurement aid: read `nbytes` (default: all) bytes of `src` with the
+    attention kernels' streaming loads; `sink` (int32, one per workgroup)
+    receives one word per workgroup. Asynchronous on the current stream."""
+    _require(src, "src")
+    _require(sink, "sink", dtype=torch.int32, ndim=1)
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    st = lib().mvk_stream_read_probe(src.data_ptr(), n, sink.data_ptr(), sink.numel(),
+                                     _stream(src, sink))
+    _check("mvk_stream_read_probe", st)
 
 
 def multi_query_workspace_size(num_seqs: int, num_query_tokens: int, max_query_len: int,

@@ -3,7 +3,8 @@
     python -m paged_kv_cache_206_amd.build          # or build() from Python
 
 Every .hip file under csrc/ is compiled with hipcc for gfx950 only, every
-.cpp file (host-only code) with g++, and all are linked into
+.cpp file (host-only code) with g++ (one compiler process per file, in
+parallel), and all are linked into
 paged_kv_cache_206_amd/libmvk.so. Packed-fp32 instructions are disabled
 (-packed-fp32-ops) for all device code.
 """
@@ -15,6 +16,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -43,35 +45,52 @@ COMMON_FLAGS = [
 FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
 
 
+def _jobs() -> int:
+    """Parallel compiler processes: MAX_JOBS if set, else the CPUs this process
+    may use (at most 16)."""
+    env = os.environ.get("MAX_JOBS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def build(verbose: bool = False, defines=()) -> str:
-    """Compile every source and link libmvk.so; returns its path. `defines`
-    adds -D flags (MVK_TUNING builds a variant whose planner honours the
-    MVK_TUNE_P / MVK_TUNE_W environment variables, for tuning sweeps)."""
+    """Compile every source (in parallel, one compiler process per file) and
+    link libmvk.so; returns its path. `defines` adds -D flags."""
     cc = hipcc()
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     host_sources = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))  # host-only C++
     if not sources:
         raise RuntimeError(f"no HIP sources under {CSRC}")
     with tempfile.TemporaryDirectory(prefix="mvk_build_") as tmp:
-        objs = []
+        cmds, objs = [], []
         for src in sources:
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [cc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []),
-                   *("-D" + d for d in defines), "-I", os.path.join(ROOT, "include"),
-                   "-c", src, "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+            cmds.append([cc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []),
+                         *("-D" + d for d in defines), "-I", os.path.join(ROOT, "include"),
+                         "-c", src, "-o", obj])
             objs.append(obj)
         for src in host_sources:
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [shutil.which("g++") or "g++", "-O2", "-std=c++17", "-fPIC", "-Wall",
-                   *("-D" + d for d in defines), "-I", os.path.join(ROOT, "include"), "-c", src,
-                   "-o", obj]
+            cmds.append([shutil.which("g++") or "g++", "-O2", "-std=c++17", "-fPIC", "-Wall",
+                         *("-D" + d for d in defines), "-I", os.path.join(ROOT, "include"),
+                         "-c", src, "-o", obj])
+            objs.append(obj)
+
+        def compile_one(cmd):
             if verbose:
                 print(" ".join(cmd), flush=True)
-            subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
-            objs.append(obj)
+            return subprocess.run(cmd, stderr=None if verbose else subprocess.PIPE)
+
+        with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            results = list(pool.map(compile_one, cmds))
+        for cmd, r in zip(cmds, results):
+            if r.returncode != 0:
+                raise subprocess.CalledProcessError(r.returncode, cmd, stderr=r.stderr)
         tmp_lib = LIB + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         if verbose:

@@ -2,9 +2,7 @@
 // Nothing here touches the GPU before every argument has been checked.
 #include <math.h>
 #include <stdint.h>
-#ifdef MVK_TUNING
-#include <stdlib.h>
-#endif
+
 
 #include "mvk.h"
 #include "launch.h"
@@ -74,7 +72,6 @@ struct Plan {
   int32_t partition_tokens;
   int32_t num_parts;
   int32_t waves;
-  int32_t head_fastest;
   int32_t longest_first;
   int32_t detect_shared;
   bool work_list;
@@ -110,24 +107,13 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   }
   // a function of the partition length alone, so that a caller passing the
   // length the library chose gets the same plan
-  int32_t waves = default_waves(p);
-  int32_t head_fastest = 0;
-  int merge_mode = -1;  // -1: chosen below
-#ifdef MVK_TUNING
-  if (getenv("MVK_TUNE_MERGE")) merge_mode = atoi(getenv("MVK_TUNE_MERGE")) != 0;
-  if (getenv("MVK_TUNE_ORDER")) head_fastest = atoi(getenv("MVK_TUNE_ORDER"));
-  if (!partition_tokens && getenv("MVK_TUNE_P")) p = atoi(getenv("MVK_TUNE_P"));
-  if (getenv("MVK_TUNE_W")) waves = atoi(getenv("MVK_TUNE_W"));
-  if (p < kBlock || p > kMaxPartition || p % kBlock || (waves != 4 && waves != 8))
-    return MVK_ERR_INVALID_ARGUMENT;
-#endif
+  const int32_t waves = default_waves(p);
   int64_t parts = ((int64_t)max_context_len + p - 1) / p;
   if (parts < 1) parts = 1;
   if (parts > kMaxGridYZ) return MVK_ERR_INVALID_ARGUMENT;  // grid z
   plan->partition_tokens = p;
   plan->num_parts = (int32_t)parts;
   plan->waves = waves;
-  plan->head_fastest = head_fastest;
   plan->partial_bytes =
       parts > 1 ? (size_t)num_seqs * num_q_heads * (size_t)parts * (size_t)(head_dim + 2) * 4u : 0;
   const int64_t dense = (int64_t)num_seqs * parts * num_kv_heads;
@@ -146,7 +132,7 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   // 363 us).
   plan->detect_shared = parts > 1 && !plan->work_list;
   plan->longest_first = parts == 1 && num_seqs <= mvk::kMaxOrderedSeqs &&
-                        max_context_len >= kMinOrderedContext && !head_fastest;
+                        max_context_len >= kMinOrderedContext;
   if (!plan->work_list && dense > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
   const int64_t per_head = (kListWorkgroups + num_kv_heads - 1) / num_kv_heads;
   plan->list_workgroups = (int32_t)(per_head < num_seqs * parts ? per_head : num_seqs * parts);
@@ -155,7 +141,7 @@ int32_t check_sizes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
   // makes every partition wait for its partial state to reach memory; that
   // pays off when few sequences are split, i.e. in work-list mode, and costs
   // more than it saves when every sequence is split (dense grids).
-  const bool merge_in_kernel = merge_mode < 0 ? plan->work_list : merge_mode != 0;
+  const bool merge_in_kernel = plan->work_list;
   plan->counter_bytes = parts > 1 ? kCounterRegion : 0;
   plan->use_counters = parts > 1 && merge_in_kernel &&
                        (size_t)num_seqs * num_kv_heads * 4u <= kCounterRegion;
@@ -214,13 +200,7 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
   // kernel holds about 230 VGPRs (two waves per SIMD), and eight-wave
   // workgroups measured slower on long contexts (Llama-7B shape, 4096-token
   // partitions: 652 vs 623 us with 5 new tokens).
-  int32_t waves = 4;
-#ifdef MVK_TUNING
-  if (!partition_tokens && getenv("MVK_TUNE_P")) p = atoi(getenv("MVK_TUNE_P"));
-  if (getenv("MVK_TUNE_W")) waves = atoi(getenv("MVK_TUNE_W"));
-  if (p < kBlock || p > kMaxPartition || p % kBlock || (waves != 4 && waves != 8))
-    return MVK_ERR_INVALID_ARGUMENT;
-#endif
+  const int32_t waves = 4;
   int64_t parts = ((int64_t)max_context_len + p - 1) / p;
   if (parts < 1) parts = 1;
   if (units * num_kv_heads * parts > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;  // 1-D grid
@@ -241,70 +221,15 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
   return MVK_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-int32_t mvk_abi_version(void) { return MVK_ABI_VERSION; }
-
-const char* mvk_status_string(int32_t status) {
-  switch (status) {
-    case MVK_OK: return "ok";
-    case MVK_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case MVK_ERR_UNSUPPORTED: return "unsupported configuration";
-    case MVK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
-    case MVK_ERR_HIP: return "HIP error";
-    case MVK_ERR_OUT_OF_BLOCKS: return "not enough free KV blocks";
-    default: return "unknown status";
-  }
-}
-
-int32_t mvk_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
-                              const int32_t* slot_mapping, int32_t num_tokens,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                              int32_t num_blocks, int32_t dtype, void* stream) {
-  if (dtype != MVK_F16 && dtype != MVK_BF16) return MVK_ERR_INVALID_ARGUMENT;
-  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return MVK_ERR_INVALID_ARGUMENT;
-  if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return MVK_ERR_UNSUPPORTED;
-  if ((int64_t)num_blocks * kBlock > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
-  if (num_tokens == 0) return MVK_OK;
-  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return MVK_ERR_INVALID_ARGUMENT;
-  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned4(slot_mapping))
-    return MVK_ERR_INVALID_ARGUMENT;
-  if (k_cache == v_cache) return MVK_ERR_INVALID_ARGUMENT;
-  const int64_t row_vecs = (int64_t)num_kv_heads * head_dim * 2 / 16;
-  if (row_vecs > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
-  hipError_t err = mvk::launch_cache_write(key, value, k_cache, v_cache, slot_mapping, num_tokens,
-                                           (int32_t)row_vecs, (int64_t)num_blocks * kBlock,
-                                           (hipStream_t)stream);
-  return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
-}
-
-int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
-                                           int32_t num_kv_heads, int32_t head_dim,
-                                           int32_t max_context_len, int32_t partition_tokens,
-                                           size_t* workspace_bytes,
-                                           int32_t* chosen_partition_tokens) {
-  if (!workspace_bytes) return MVK_ERR_INVALID_ARGUMENT;
-  Plan plan{};
-  const int32_t st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                                 partition_tokens, &plan);
-  if (st != MVK_OK) return st;
-  *workspace_bytes = plan.workspace_bytes;
-  if (chosen_partition_tokens) *chosen_partition_tokens = plan.partition_tokens;
-  return MVK_OK;
-}
-
-int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void* v_cache,
-                                   const int32_t* block_tables, const int32_t* context_lens,
-                                   const void* new_key, const void* new_value,
-                                   const int32_t* slot_mapping, int32_t num_seqs,
-                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t block_size, int32_t num_blocks,
-                                   int32_t max_blocks_per_seq, int32_t max_context_len,
-                                   float scale, int32_t dtype, int32_t partition_tokens,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+int32_t decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, const void* new_key,
+                    const void* new_value, const int32_t* slot_mapping, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, float scale, int32_t dtype,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
   if (dtype != MVK_F16 && dtype != MVK_BF16) return MVK_ERR_INVALID_ARGUMENT;
   if (block_size != kBlock) return MVK_ERR_UNSUPPORTED;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale))
@@ -361,13 +286,98 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
   a.partition_tokens = plan.partition_tokens;
   a.num_parts = plan.num_parts;
   a.waves = plan.waves;
-  a.head_fastest = plan.head_fastest;
   a.longest_first = plan.longest_first;
   a.detect_shared = plan.detect_shared;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;
-  hipError_t err = mvk::launch_paged_decode(a, (hipStream_t)stream);
+  hipError_t err = mvk::launch_paged_decode(a, stream);
   return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mvk_abi_version(void) { return MVK_ABI_VERSION; }
+
+const char* mvk_status_string(int32_t status) {
+  switch (status) {
+    case MVK_OK: return "ok";
+    case MVK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MVK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MVK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MVK_ERR_HIP: return "HIP error";
+    case MVK_ERR_OUT_OF_BLOCKS: return "not enough free KV blocks";
+    default: return "unknown status";
+  }
+}
+
+int32_t mvk_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                              const int32_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t dtype, void* stream) {
+  if (dtype != MVK_F16 && dtype != MVK_BF16) return MVK_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return MVK_ERR_INVALID_ARGUMENT;
+  if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return MVK_ERR_UNSUPPORTED;
+  if ((int64_t)num_blocks * kBlock > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return MVK_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return MVK_ERR_INVALID_ARGUMENT;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(slot_mapping))
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (k_cache == v_cache) return MVK_ERR_INVALID_ARGUMENT;
+  const int64_t row_vecs = (int64_t)num_kv_heads * head_dim * 2 / 16;
+  if (row_vecs > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
+  hipError_t err = mvk::launch_cache_write(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                           (int32_t)row_vecs, (int64_t)num_blocks * kBlock,
+                                           (hipStream_t)stream);
+  return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
+}
+
+size_t mvk_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t head_dim, int32_t max_context_len) {
+  size_t most = 0;
+  bool any = false;
+  for (int32_t g = 1; g <= 8; g *= 2) {
+    if (num_q_heads <= 0 || num_q_heads % g != 0) continue;
+    Plan plan{};
+    if (check_sizes(num_seqs, num_q_heads, num_q_heads / g, head_dim, max_context_len, 0, &plan) !=
+        MVK_OK)
+      continue;
+    any = true;
+    if (plan.workspace_bytes > most) most = plan.workspace_bytes;
+  }
+  return any ? most : SIZE_MAX;
+}
+
+int32_t mvk_paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t max_context_len, int32_t partition_tokens,
+                                           size_t* workspace_bytes,
+                                           int32_t* chosen_partition_tokens) {
+  if (!workspace_bytes) return MVK_ERR_INVALID_ARGUMENT;
+  Plan plan{};
+  const int32_t st = check_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                 partition_tokens, &plan);
+  if (st != MVK_OK) return st;
+  *workspace_bytes = plan.workspace_bytes;
+  if (chosen_partition_tokens) *chosen_partition_tokens = plan.partition_tokens;
+  return MVK_OK;
+}
+
+int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const void* new_key, const void* new_value,
+                                   const int32_t* slot_mapping, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len,
+                                   float scale, int32_t dtype, int32_t partition_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, new_key, new_value,
+                     slot_mapping, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                     partition_tokens, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int32_t mvk_paged_attention_multi_query_workspace_size(
@@ -462,6 +472,10 @@ int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const v
     return MVK_ERR_INVALID_ARGUMENT;
   if (num_q_heads % num_kv_heads != 0) return MVK_ERR_INVALID_ARGUMENT;
   if (!mvk::decode_supported(head_dim, num_q_heads / num_kv_heads)) return MVK_ERR_UNSUPPORTED;
+  // The prefill kernel takes the running maximum of the raw dot products and
+  // scales it afterwards, which is the maximum of the scaled logits only for
+  // a positive scale.
+  if (!(scale > 0.0f)) return MVK_ERR_UNSUPPORTED;
   if ((int64_t)num_tokens > (int64_t)num_seqs * max_seqlen) return MVK_ERR_INVALID_ARGUMENT;
   // a prompt's K/V rows are addressed with 32-bit byte offsets
   if (((int64_t)max_seqlen + 256) * num_kv_heads * head_dim * 2 > INT32_MAX)
@@ -498,6 +512,16 @@ int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const v
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;
   hipError_t err = mvk::launch_prefill(a, (hipStream_t)stream);
+  return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
+}
+
+int32_t mvk_stream_read_probe(const void* src, size_t bytes, void* sink, int32_t workgroups,
+                              void* stream) {
+  if (!src || !sink || !aligned16(src) || !aligned4(sink)) return MVK_ERR_INVALID_ARGUMENT;
+  if (bytes < 16 || bytes % 16 || bytes > (size_t(1) << 31)) return MVK_ERR_INVALID_ARGUMENT;
+  if (workgroups < 1 || workgroups > kMaxGridYZ) return MVK_ERR_INVALID_ARGUMENT;
+  const hipError_t err = mvk::launch_stream_read(src, (uint32_t)bytes, (uint32_t*)sink, workgroups,
+                                                 (hipStream_t)stream);
   return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
 }
 

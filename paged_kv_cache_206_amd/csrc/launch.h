@@ -8,6 +8,12 @@
 
 namespace mvk {
 
+// Read-only streaming probe over [src, src + bytes) (bytes < 4 GiB, a multiple
+// of 16) with `workgroups` workgroups of 256 threads; workgroup i stores one
+// word to sink[i].
+hipError_t launch_stream_read(const void* src, uint32_t bytes, uint32_t* sink, int32_t workgroups,
+                              hipStream_t stream);
+
 hipError_t launch_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                               const int32_t* slot_mapping, int32_t num_tokens, int32_t row_vecs,
                               int64_t num_slots, hipStream_t stream);
@@ -32,7 +38,6 @@ struct DecodeArgs {
   int32_t num_blocks, max_blocks_per_seq, max_context_len;
   int32_t partition_tokens, num_parts;
   int32_t waves;     // waves per workgroup (4 or 8)
-  int32_t head_fastest;  // grid order (see Shape)
   int32_t longest_first; // single-pass grid dispatched longest sequence first (see Shape)
   int32_t detect_shared; // blocks shared with a neighbouring sequence keep the default cache policy
   int32_t* items;    // work list (count, one dispatch counter per KV head, then (seq, part)

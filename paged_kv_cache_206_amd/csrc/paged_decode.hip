@@ -57,7 +57,6 @@ struct Shape {
   int32_t num_seqs;
   int32_t num_kv_heads, num_blocks, max_blocks, max_context_len, partition_tokens, num_parts;
   float scale_log2;
-  int32_t head_fastest;  // grid order: 1 = (KV head, sequence, partition), 0 = (sequence, KV head, partition)
   int32_t longest_first; // single-pass grids of <= kMaxOrderedSeqs sequences: (rank, KV head) in dispatch order
 };
 
@@ -460,8 +459,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kMinWave
       part = 0;
     } else {
       const uint32_t v = xcd_contiguous(i, n);
-      s = sh.head_fastest ? (v / H) % S : v % S;
-      h = sh.head_fastest ? v % H : (v / S) % H;
+      s = v % S;
+      h = (v / S) % H;
       part = v / (S * H);
     }
     decode_item<DT, D, G, W, NPF, USE_MFMA, FUSED, SHARED>(s, h, part, out, ws_ml, ws_o, q, k_cache, v_cache,
@@ -630,7 +629,7 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_kernel(
 template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED, bool SHARED>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   Shape sh{a.num_seqs, a.num_kv_heads, a.num_blocks, a.max_blocks_per_seq, a.max_context_len,
-           a.partition_tokens, a.num_parts, a.scale_log2, a.head_fastest, a.longest_first};
+           a.partition_tokens, a.num_parts, a.scale_log2, a.longest_first};
   dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_parts);
   if (a.items != nullptr) {
     hipLaunchKernelGGL(paged_decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.items,

@@ -30,7 +30,8 @@ def mvk():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "mvk_abi_version", "mvk_status_string", "mvk_reshape_and_cache",
-        "mvk_paged_attention_workspace_size", "mvk_paged_attention_decode",
+        "mvk_paged_attention_workspace_size", "mvk_paged_attention_workspace_bytes",
+        "mvk_paged_attention_decode", "mvk_stream_read_probe",
         "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query",
         "mvk_prefill_attention",
         "mvk_bm_create", "mvk_bm_destroy", "mvk_bm_num_free", "mvk_bm_can_admit", "mvk_bm_admit",
@@ -52,7 +53,7 @@ def test_single_hip_runtime_mapped(mvk):
 
 
 def test_version_and_status_strings(mvk):
-    assert mvk.abi_version() == 5
+    assert mvk.abi_version() == 6
     assert mvk.status_string(0) == "ok"
     assert mvk.status_string(3) == "workspace too small"
     assert mvk.status_string(5) == "not enough free KV blocks"
@@ -147,6 +148,20 @@ def test_workspace_size(mvk):
         mvk.workspace_size(2, 3, 2, 64, 10)
 
 
+def test_workspace_bytes_bounds_every_kv_head_count(mvk):
+    """The KV-head-free workspace query is the largest exact size over the
+    supported group sizes, and SIZE_MAX (an exception here) for invalid sizes."""
+    for S, hq, d, L in [(4, 4, 64, 45), (32, 32, 128, 32768), (512, 16, 128, 131072),
+                        (60, 16, 128, 256), (7, 8, 64, 5000)]:
+        exact = [mvk.workspace_size(S, hq, hq // g, d, L)[0] for g in (1, 2, 4, 8) if hq % g == 0]
+        assert mvk.workspace_bytes(S, hq, d, L) == max(exact)
+    assert mvk.workspace_bytes(60, 16, 128, 256) == 0
+    with pytest.raises(mvk.MvkError):
+        mvk.workspace_bytes(4, 4, 96, 45)
+    with pytest.raises(mvk.MvkError):
+        mvk.workspace_bytes(-1, 4, 64, 45)
+
+
 def test_library_partition_choice(mvk):
     """The partition lengths the planner picks for the benchmark's shapes: a
     single pass for short and medium contexts, 4096 tokens for a dense grid
@@ -239,6 +254,9 @@ def prefill_call(mvk, **over):
     (dict(kc=None), 1),
     (dict(nb=0), 1),
     (dict(maxlen=4_194_304), 2),      # rows past 32-bit byte offsets
+    (dict(scale=0.0), 2),             # only a positive scale is supported
+    (dict(scale=-0.1), 2),
+    (dict(scale=-0.0), 2),
 ])
 def test_prefill_validation(mvk, over, status):
     assert prefill_call(mvk, **over) == status
@@ -248,6 +266,15 @@ def test_prefill_noop(mvk):
     assert prefill_call(mvk, S=0, T=0, out=None, q=None) == 0
     assert prefill_call(mvk, T=0, out=None, q=None) == 0
 
+
+
+@pytest.mark.parametrize("over", [
+    dict(src=None), dict(sink=None), dict(src=FAKE + 4), dict(nbytes=0), dict(nbytes=24),
+    dict(nbytes=(1 << 31) + 16), dict(wg=0), dict(wg=70000)])
+def test_stream_probe_validation(mvk, over):
+    a = dict(src=FAKE, nbytes=1 << 20, sink=FAKE * 2, wg=256)
+    a.update(over)
+    assert mvk.lib().mvk_stream_read_probe(a["src"], a["nbytes"], a["sink"], a["wg"], None) == 1
 
 
 def test_tensors_on_different_devices_are_rejected(mvk):
