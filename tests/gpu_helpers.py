@@ -1,4 +1,7 @@
 """Shared helpers for the GPU parity tests (oracle on the host, library on the GPU)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -46,3 +49,29 @@ def max_err(gpu_out, ref, dtype, seqs=None):
         g = g[np.asarray(seqs)]
     assert np.all(np.isfinite(g)), "non-finite GPU output"
     return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def host_threads() -> int:
+    """Host threads for spreading the oracle over sequences (the CPUs this
+    process may use, at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def oracle_decode_all(q, kc, vc, block_tables, context_lens, scale, dtype, seqs=None):
+    """The fp64 decode oracle over every sequence (or `seqs`), its sequences
+    split into chunks that run in a thread pool; each chunk is one call of
+    oracle.paged_decode, so the result is the oracle's, row for row."""
+    bt = np.asarray(block_tables)
+    cl = np.asarray(context_lens)
+    idx = np.arange(q.shape[0]) if seqs is None else np.asarray(seqs)
+    chunks = [c for c in np.array_split(idx, max(1, min(len(idx), 4 * host_threads()))) if len(c)]
+
+    def run(c):
+        return oracle.paged_decode(q[c], kc, vc, bt[c], cl[c], scale, dtype)
+    with ThreadPoolExecutor(host_threads()) as ex:
+        parts = list(ex.map(run, chunks))
+    return np.concatenate(parts, axis=0) if parts else np.zeros((0,) + q.shape[1:])

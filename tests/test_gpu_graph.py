@@ -1,11 +1,16 @@
-"""Captured HIP graphs of the decode step (cache write + decode per layer)
-replay bit-identically to eager calls. Every replay is preceded by eager work
-and a synchronisation and is checked against the eager result."""
+"""Captured HIP graphs of the decode step (cache write + decode per layer),
+of multi-query calls and of a prefill call: every replay is preceded by eager
+work and a synchronisation, and every replayed output is checked against the
+fp64 oracle at the parity tolerance (the pools bit for bit against the
+oracle's cache write) as well as bit for bit against the eager result."""
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_206_amd as mvk
 import workloads as W
+from gpu_helpers import TOL, bits, max_err
 
 pytestmark = pytest.mark.gpu
 
@@ -40,6 +45,14 @@ def test_graph_replay_matches_eager(case, fused):
                            layers=2)
         p = 32
     maxlen = wl.max_context_len          # host-side, before anything is captured
+    # oracle: each layer's cache write, then decode over the written pools
+    refs, pools = [], []
+    for l in wl.layers:
+        kc, vc = oracle.cache_write(bits(l.k_cache), bits(l.v_cache), bits(l.key), bits(l.value),
+                                    wl.slot_mapping.numpy())
+        pools.append((kc, vc))
+        refs.append(oracle.paged_decode(bits(l.q), kc, vc, wl.block_tables.numpy(),
+                                        wl.context_lens.numpy(), wl.scale, wl.dtype))
     wl = wl.to("cuda")
     bt, cl, slots = wl.block_tables, wl.context_lens, wl.slot_mapping
     nbytes, _ = mvk.workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
@@ -66,14 +79,21 @@ def test_graph_replay_matches_eager(case, fused):
         (x @ x).sum().item()           # unrelated eager work, then a sync
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip(eager, graphed):
+        for li, (a, b) in enumerate(zip(eager, graphed)):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (case, rep)
+            err = max_err(b, refs[li], wl.dtype)
+            assert err <= TOL[wl.dtype], (case, rep, li, err)
+        for l, (kc, vc) in zip(wl.layers, pools):   # the replayed writes land as the oracle's
+            assert np.array_equal(bits(l.k_cache), kc) and np.array_equal(bits(l.v_cache), vc)
+    print(f"graph {case} fused={fused}: 3 replays x {len(refs)} layers match eager bitwise and "
+          f"the oracle (last max abs err {err:.3e})", flush=True)
 
 
-def replay_and_check(capture, prepare, pairs, label):
+def replay_and_check(capture, prepare, pairs, label, check=None):
     """Warm up on a side stream, capture, then replay three times, each after
     prepare() (clobbering the outputs), unrelated eager work and a sync,
-    comparing every (eager, graphed) pair bit for bit."""
+    comparing every (eager, graphed) pair bit for bit and calling check()
+    (the oracle comparison) after every replay."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -91,6 +111,8 @@ def replay_and_check(capture, prepare, pairs, label):
         torch.cuda.synchronize()
         for a, b in pairs:
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (label, rep)
+        if check is not None:
+            check(rep)
 
 
 @pytest.mark.parametrize("partition_tokens", [0, 64], ids=["single_pass", "split_merge"])
@@ -99,6 +121,10 @@ def test_multi_query_graph_replay_matches_eager(partition_tokens):
     wl = W.make_custom("g", "bf16", lens, 16, 4, 128, sum(-(-L // 16) for L in lens) + 4, 31)
     q, qs = W.make_queries(wl, [5, 3, 7, 2, 6], seed=32)
     maxlen, maxq = wl.max_context_len, 7
+    lc = wl.layers[0]
+    ref = oracle.paged_multi_query(bits(q), bits(lc.k_cache), bits(lc.v_cache),
+                                   wl.block_tables.numpy(), wl.context_lens.numpy(), qs.numpy(),
+                                   wl.scale, wl.dtype)
     wl, q, qs = wl.to("cuda"), q.to("cuda"), qs.to("cuda")
     layer = wl.layers[0]
     nbytes, _ = mvk.multi_query_workspace_size(wl.num_seqs, q.shape[0], maxq, wl.num_q_heads,
@@ -115,13 +141,20 @@ def test_multi_query_graph_replay_matches_eager(partition_tokens):
     call(eager)
     torch.cuda.synchronize()
     graphed = torch.empty_like(q)
+    def check(rep):
+        err = max_err(graphed, ref, "bf16")
+        assert err <= TOL["bf16"], (partition_tokens, rep, err)
     replay_and_check(lambda: call(graphed), lambda: graphed.fill_(float("nan")),
-                     [(eager, graphed)], f"mq p={partition_tokens}")
+                     [(eager, graphed)], f"mq p={partition_tokens}", check)
 
 
 def test_prefill_graph_replay_matches_eager():
     pf = W.make_prefill("f16", [200, 17, 64, 129], 16, 2, 64, seed=33)
     maxlen = pf.max_seqlen
+    ref = oracle.prefill_attention(bits(pf.q), bits(pf.key), bits(pf.value), pf.cu_seqlens.numpy(),
+                                   pf.scale, "f16")
+    kc_ref, vc_ref = oracle.cache_write(bits(pf.k_cache), bits(pf.v_cache), bits(pf.key),
+                                        bits(pf.value), pf.slot_mapping.numpy())
     g = pf.to("cuda")
     k0, v0 = g.k_cache.clone(), g.v_cache.clone()
 
@@ -140,6 +173,11 @@ def test_prefill_graph_replay_matches_eager():
         g.k_cache.copy_(k0)
         g.v_cache.copy_(v0)
         graphed.fill_(float("nan"))
+    def check(rep):
+        err = max_err(graphed, ref, "f16")
+        assert err <= TOL["f16"], (rep, err)
+        assert np.array_equal(bits(g.k_cache), kc_ref) and np.array_equal(bits(g.v_cache), vc_ref)
     prepare()
     replay_and_check(lambda: call(graphed), prepare,
-                     [(eager, graphed), (k_eager, g.k_cache), (v_eager, g.v_cache)], "prefill")
+                     [(eager, graphed), (k_eager, g.k_cache), (v_eager, g.v_cache)], "prefill",
+                     check)
