@@ -22,7 +22,8 @@
  *
  * Conventions shared by every entry point
  *   - Pointers to tensors are DEVICE pointers owned by the caller. The library
- *     allocates nothing, keeps no state between calls and is thread-safe.
+ *     allocates nothing and keeps no state between calls (the one exception is
+ *     mvk_paged_attention_decode_noalloc's static scratch), and is thread-safe.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     asynchronously; MVK_OK means "arguments valid and kernels launched".
  *     A fault inside a kernel surfaces at the caller's next synchronisation.
@@ -58,7 +59,9 @@ typedef enum mvk_status {
     MVK_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, group size, block size */
     MVK_ERR_WORKSPACE_TOO_SMALL = 3,
     MVK_ERR_HIP = 4,                /* a HIP launch reported an error */
-    MVK_ERR_OUT_OF_BLOCKS = 5       /* block manager: not enough free KV blocks */
+    MVK_ERR_OUT_OF_BLOCKS = 5,      /* block manager: not enough free KV blocks */
+    MVK_ERR_SCRATCH_LIMIT = 6       /* allocation-free call: the sizes need more than the
+                                       library's static scratch (mvk_paged_attention_scratch_limit) */
 } mvk_status;
 
 typedef enum mvk_dtype {
@@ -204,6 +207,44 @@ int32_t mvk_paged_attention_decode(void* out, const void* q,
                                    int32_t max_blocks_per_seq, int32_t max_context_len,
                                    float scale, int32_t dtype, int32_t partition_tokens,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mvk_paged_attention_decode_noalloc - mvk_paged_attention_decode without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, semantics, kernels and output bits as
+ * mvk_paged_attention_decode with the same partition_tokens; the partial
+ * states, partition counters and work list that a split call keeps in the
+ * workspace go to a static device array of the library instead
+ * (mvk_paged_attention_scratch_limit() bytes per GPU, held from the first such
+ * call on a GPU until the process ends). The call allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine.
+ *   - Every call on one GPU shares that GPU's array. Calls that may overlap on
+ *     one GPU (different streams without ordering, several threads) race on it
+ *     and give unspecified results; calls ordered on one stream are safe.
+ *   - The first call on a GPU also enqueues, on `stream`, a kernel that clears
+ *     the counter region of the array; every completed call leaves the
+ *     counters at zero again.
+ * Errors: as mvk_paged_attention_decode, with MVK_ERR_SCRATCH_LIMIT (nothing
+ * launched) when these sizes would need a larger workspace than the array
+ * (mvk_paged_attention_workspace_size gives the need), and MVK_ERR_HIP when the
+ * array's device address cannot be obtained.
+ */
+int32_t mvk_paged_attention_decode_noalloc(void* out, const void* q,
+                                           void* k_cache, void* v_cache,
+                                           const int32_t* block_tables, const int32_t* context_lens,
+                                           const void* new_key, const void* new_value,
+                                           const int32_t* slot_mapping,
+                                           int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t num_blocks,
+                                           int32_t max_blocks_per_seq, int32_t max_context_len,
+                                           float scale, int32_t dtype, int32_t partition_tokens,
+                                           void* stream);
+
+/* Bytes of the static per-GPU scratch array of mvk_paged_attention_decode_noalloc. */
+size_t mvk_paged_attention_scratch_limit(void);
 
 /*
  * mvk_paged_attention_multi_query_workspace_size - bytes of scratch that

@@ -9,7 +9,10 @@ is no fallback: if libmvk.so is missing, the first call fails with instructions.
                            max_context_len=None, out=None, partition_tokens=0,
                            workspace=None, new_key=None, new_value=None,
                            slot_mapping=None)
-    workspace_size(...), workspace_bytes(...)
+    paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens,
+                                   scale, max_context_len, out, partition_tokens=0,
+                                   new_key=None, new_value=None, slot_mapping=None)
+    workspace_size(...), workspace_bytes(...), scratch_limit()
     paged_attention_multi_query(q, k_cache, v_cache, block_tables, context_lens,
                                 query_start, scale, max_query_len=None,
                                 max_context_len=None, out=None, partition_tokens=0,
@@ -39,6 +42,7 @@ MVK_ERR_UNSUPPORTED = 2
 MVK_ERR_WORKSPACE_TOO_SMALL = 3
 MVK_ERR_HIP = 4
 MVK_ERR_OUT_OF_BLOCKS = 5
+MVK_ERR_SCRATCH_LIMIT = 6
 MVK_F16 = 0
 MVK_BF16 = 1
 
@@ -59,6 +63,11 @@ SIGNATURES = {
                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int, _c_int, _c_float, _c_int, _c_int, _ptr,
                                             _c_size, _ptr]),
+    "mvk_paged_attention_decode_noalloc": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                                    _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                                    _c_int, _c_int, _c_int, _c_float, _c_int,
+                                                    _c_int, _ptr]),
+    "mvk_paged_attention_scratch_limit": (_c_size, []),
     "mvk_stream_read_probe": (_c_int, [_ptr, _c_size, _ptr, _c_int, _ptr]),
     "mvk_paged_attention_multi_query_workspace_size": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -208,6 +217,11 @@ def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_
     return n
 
 
+def scratch_limit() -> int:
+    """Bytes of the static per-GPU scratch of paged_attention_decode_noalloc."""
+    return lib().mvk_paged_attention_scratch_limit()
+
+
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
                  new_key, new_value, slot_mapping):
     """Checks shared by the two decode entry points; returns the pieces of the
@@ -285,6 +299,35 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                                   context_lens, new_key, new_value, slot_mapping,
                                                   workspace))
     _check("mvk_paged_attention_decode", st)
+    return out
+
+
+def paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, scale: float,
+                                   max_context_len: int, out: torch.Tensor,
+                                   partition_tokens: int = 0,
+                                   new_key: torch.Tensor | None = None,
+                                   new_value: torch.Tensor | None = None,
+                                   slot_mapping: torch.Tensor | None = None) -> torch.Tensor:
+    """paged_attention_decode without a workspace: the library keeps split
+    partitions' partial states in its static per-GPU scratch
+    (scratch_limit() bytes; larger needs raise MvkError with
+    MVK_ERR_SCRATCH_LIMIT). `max_context_len` and `out` are required, so that
+    the call neither synchronises nor allocates. Calls that may overlap on one
+    GPU race on the shared scratch."""
+    if max_context_len is None or out is None:
+        raise ValueError("paged_attention_decode_noalloc needs max_context_len and out")
+    S, hq, hkv, d, nb, bs, nk, nv, sm, max_context_len, out = _decode_args(
+        q, k_cache, v_cache, block_tables, context_lens, max_context_len, out, new_key,
+        new_value, slot_mapping)
+    st = lib().mvk_paged_attention_decode_noalloc(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), nk, nv, sm, S, hq, hkv, d, bs, nb,
+        block_tables.shape[1], max_context_len, float(scale), _dtype_code(q), partition_tokens,
+        _stream(q, out, k_cache, v_cache, block_tables, context_lens, new_key, new_value,
+                slot_mapping))
+    _check("mvk_paged_attention_decode_noalloc", st)
     return out
 
 

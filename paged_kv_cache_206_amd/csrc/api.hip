@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "mvk.h"
 #include "launch.h"
@@ -222,6 +223,50 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
 }
 
 
+// ------------------------------------------- static scratch (allocation-free calls)
+// The allocation-free decode entry point keeps its partial states, partition
+// counters and work list in this array instead of a caller workspace. Every
+// GPU the library runs on holds its own copy until the process ends. In host
+// code the name `scratch` is only a host-side stand-in for the symbol: its
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the GPU that `stream` runs on
+// (the current device for the NULL stream). The first call on a device also
+// enqueues, on `stream`, a kernel that zero-fills the counter region at its
+// start (the partition counters must start at zero; every completed call
+// leaves them at zero again).
+hipError_t scratch_for_stream(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t err = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    err = hipGetDevice(&cur);
+    if (err != hipSuccess) return err;
+    if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return err;
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err == hipSuccess) err = mvk::launch_zero_fill(p, kCounterRegion, stream);
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (err == hipSuccess) err = back;
+    }
+    if (err != hipSuccess) return err;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 int32_t decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, const void* new_key,
                     const void* new_value, const int32_t* slot_mapping, int32_t num_seqs,
@@ -229,7 +274,7 @@ int32_t decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
                     int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                     int32_t max_context_len, float scale, int32_t dtype,
                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+                    hipStream_t stream, bool use_scratch) {
   if (dtype != MVK_F16 && dtype != MVK_BF16) return MVK_ERR_INVALID_ARGUMENT;
   if (block_size != kBlock) return MVK_ERR_UNSUPPORTED;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale))
@@ -255,8 +300,18 @@ int32_t decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
     if ((int64_t)num_blocks * kBlock > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
   }
   if (plan.workspace_bytes > 0) {
-    if (!workspace || workspace_bytes < plan.workspace_bytes) return MVK_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned16(workspace)) return MVK_ERR_INVALID_ARGUMENT;
+    if (use_scratch) {
+      // allocation-free entry point: the library's static per-GPU scratch
+      if (plan.workspace_bytes > kScratchBytes) return MVK_ERR_SCRATCH_LIMIT;
+      void* ptr = nullptr;
+      const hipError_t err = scratch_for_stream(stream, &ptr);
+      if (err != hipSuccess) return MVK_ERR_HIP;
+      workspace = ptr;
+      workspace_bytes = kScratchBytes;
+    } else {
+      if (!workspace || workspace_bytes < plan.workspace_bytes) return MVK_ERR_WORKSPACE_TOO_SMALL;
+      if (!aligned16(workspace)) return MVK_ERR_INVALID_ARGUMENT;
+    }
   }
 
   mvk::DecodeArgs a{};
@@ -308,6 +363,9 @@ const char* mvk_status_string(int32_t status) {
     case MVK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MVK_ERR_HIP: return "HIP error";
     case MVK_ERR_OUT_OF_BLOCKS: return "not enough free KV blocks";
+    case MVK_ERR_SCRATCH_LIMIT:
+      return "needs more scratch than the library's static per-GPU array holds "
+             "(mvk_paged_attention_scratch_limit)";
     default: return "unknown status";
   }
 }
@@ -377,8 +435,26 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, new_key, new_value,
                      slot_mapping, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
-                     partition_tokens, workspace, workspace_bytes, (hipStream_t)stream);
+                     partition_tokens, workspace, workspace_bytes, (hipStream_t)stream, false);
 }
+
+int32_t mvk_paged_attention_decode_noalloc(void* out, const void* q, void* k_cache,
+                                           void* v_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens, const void* new_key,
+                                           const void* new_value, const int32_t* slot_mapping,
+                                           int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t num_blocks,
+                                           int32_t max_blocks_per_seq, int32_t max_context_len,
+                                           float scale, int32_t dtype, int32_t partition_tokens,
+                                           void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, new_key, new_value,
+                     slot_mapping, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                     partition_tokens, nullptr, 0, (hipStream_t)stream, true);
+}
+
+size_t mvk_paged_attention_scratch_limit(void) { return kScratchBytes; }
 
 int32_t mvk_paged_attention_multi_query_workspace_size(
     int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len, int32_t num_q_heads,

@@ -8,6 +8,11 @@
 
 namespace mvk {
 
+// Zero-fills `bytes` (a multiple of 16) bytes at `dst` with a kernel on
+// `stream` (a kernel rather than a memset node, so that it can be captured
+// into a graph and replayed).
+hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t stream);
+
 // Read-only streaming probe over [src, src + bytes) (bytes < 4 GiB, a multiple
 // of 16) with `workgroups` workgroups of 256 threads; workgroup i stores one
 // word to sink[i].

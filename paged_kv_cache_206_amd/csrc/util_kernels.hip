@@ -1,9 +1,26 @@
-// A read-only streaming probe that measures the practical HBM read ceiling
-// the attention kernels are compared against.
+// Small utility kernels: a zero fill for library-owned scratch, and a
+// read-only streaming probe that measures the practical HBM read ceiling the
+// attention kernels are compared against.
 #include "device_common.h"
 #include "launch.h"
 
 namespace mvk {
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ dst, int64_t vecs) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vecs; i += stride)
+    dst[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t stream) {
+  const int64_t vecs = (int64_t)(bytes / 16);
+  if (vecs == 0) return hipSuccess;
+  int64_t blocks = (vecs + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint4*)dst,
+                     vecs);
+  return hipGetLastError();
+}
 
 // Streaming read: every thread reads kUnroll 16-byte vectors per iteration
 // (all issued before any is consumed), with the same non-temporal cache

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "mvk_abi_version", "mvk_status_string", "mvk_reshape_and_cache",
         "mvk_paged_attention_workspace_size", "mvk_paged_attention_workspace_bytes",
-        "mvk_paged_attention_decode", "mvk_stream_read_probe",
+        "mvk_paged_attention_decode", "mvk_paged_attention_decode_noalloc",
+        "mvk_paged_attention_scratch_limit", "mvk_stream_read_probe",
         "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query",
         "mvk_prefill_attention",
         "mvk_bm_create", "mvk_bm_destroy", "mvk_bm_num_free", "mvk_bm_can_admit", "mvk_bm_admit",
@@ -55,6 +56,7 @@ def test_single_hip_runtime_mapped(mvk):
 def test_version_and_status_strings(mvk):
     assert mvk.abi_version() == 6
     assert mvk.status_string(0) == "ok"
+    assert "scratch" in mvk.status_string(6)
     assert mvk.status_string(3) == "workspace too small"
     assert mvk.status_string(5) == "not enough free KV blocks"
     assert mvk.status_string(99) == "unknown status"
@@ -109,6 +111,46 @@ def test_decode_validation(mvk, over, status):
 
 def test_decode_zero_seqs_is_noop(mvk):
     assert decode_call(mvk, S=0, out=None, q=None) == 0
+
+
+def noalloc_call(mvk, **over):
+    a = dict(out=FAKE, q=FAKE * 2, k=FAKE * 3, v=FAKE * 4, bt=FAKE * 5, cl=FAKE * 6, nk=None,
+             nv=None, sm=None, S=4, hq=4, hkv=2, d=64, bs=16, nb=32, mb=4, maxlen=45,
+             scale=0.125, dtype=0, part=0, stream=None)
+    a.update(over)
+    return mvk.lib().mvk_paged_attention_decode_noalloc(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["nk"], a["nv"], a["sm"], a["S"],
+        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["maxlen"], a["scale"], a["dtype"],
+        a["part"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=2), 1),
+    (dict(d=96), 2),
+    (dict(q=None), 1),
+    (dict(out=FAKE * 2), 1),
+    (dict(scale=math.nan), 1),
+    # the skewed batch at 1024-token partitions needs far more than the static scratch
+    (dict(S=512, hq=16, hkv=8, d=128, nb=40000, mb=8192, maxlen=131072, part=1024), 6),
+])
+def test_noalloc_validation(mvk, over, status):
+    """The allocation-free entry point validates like the workspace one, and a
+    request that would need more than its static scratch is refused before
+    anything reaches HIP."""
+    assert noalloc_call(mvk, **over) == status
+
+
+def test_noalloc_zero_seqs_is_noop(mvk):
+    assert noalloc_call(mvk, S=0, out=None, q=None) == 0
+
+
+def test_scratch_limit_covers_the_split_workloads(mvk):
+    """The static scratch is 32 MiB, enough for the long-context Llama-7B-shaped
+    batch at the library's partition choice, not for the skewed batch."""
+    limit = mvk.scratch_limit()
+    assert limit == 32 << 20
+    assert mvk.workspace_size(32, 32, 8, 128, 32768)[0] <= limit
+    assert mvk.workspace_size(512, 16, 8, 128, 131072)[0] > limit
 
 
 def cache_call(mvk, **over):
