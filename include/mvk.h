@@ -209,6 +209,84 @@ int32_t mvk_paged_attention_decode(void* out, const void* q,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Planned decode: the layout of a decode step's work computed once per step
+ * and reused by every layer's decode call of that step.
+ *
+ * In steady state every running sequence is in one batched decode step, and
+ * every layer runs that step over its own pools with the same block tables,
+ * context lengths and new-token slots ("从零手写 vLLM 核心：mini-vllm 项目深度解析",
+ * "关键工程决策" items 1-3). mvk_paged_attention_plan reads those arrays once
+ * per step on the device: it ranks the sequences by length, deals the
+ * (sequence, KV head) items to workgroups that carry equal numbers of blocks
+ * (long items paired with short ones), splits each workgroup's waves over its
+ * items, and records for every wave its sequence, KV head, token range and the
+ * physical ids of its blocks. Each mvk_paged_attention_decode_planned call
+ * then starts streaming K/V after one load per wave, with no per-layer
+ * ranking or table walk.
+ *
+ * Scope: single-pass batches (each (sequence, KV head) item is done by one
+ * workgroup): at most 1024 sequences, and contexts short enough for the
+ * items of a workgroup (mvk_paged_attention_plan_size returns
+ * MVK_ERR_UNSUPPORTED otherwise; mvk_paged_attention_decode covers every
+ * batch). The plan is a snapshot: it holds copies of the block ids, lengths
+ * and slots as they are when the plan kernel runs (stream order); later
+ * changes to those arrays do not reach planned calls until the next plan.
+ */
+
+/* Bytes of device memory a plan for these sizes takes (*plan_bytes).
+ * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED (outside the planned
+ * path's scope: use mvk_paged_attention_decode). */
+int32_t mvk_paged_attention_plan_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len, size_t* plan_bytes);
+
+/*
+ * mvk_paged_attention_plan - build a step's plan into `plan` (device memory of
+ * plan_bytes >= mvk_paged_attention_plan_size; caller-owned; 16-byte
+ * aligned), asynchronously on `stream`.
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq] (device), as for decode.
+ *   context_lens  int32 [num_seqs] (device); values are clamped into
+ *                 [0, max_context_len].
+ *   slot_mapping  int32 [num_seqs] (device) or NULL: each sequence's new-token
+ *                 slot, used by planned calls that fuse the cache write.
+ *   max_context_len  host-side bound of context_lens, <= max_blocks_per_seq * 16.
+ * num_seqs == 0 is a no-op. Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED,
+ * MVK_ERR_WORKSPACE_TOO_SMALL (plan_bytes), MVK_ERR_HIP.
+ */
+int32_t mvk_paged_attention_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* slot_mapping,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq,
+                                 int32_t max_context_len, void* stream);
+
+/*
+ * mvk_paged_attention_decode_planned - one layer's decode step through a plan.
+ *
+ * Computes what mvk_paged_attention_decode computes (same definition,
+ * arithmetic and rounding) for the block tables, context lengths and slots the
+ * plan was built from; num_seqs, num_q_heads, num_kv_heads, head_dim and
+ * max_context_len must be those of the plan call. With new_key / new_value
+ * ([num_seqs, num_kv_heads, head_dim]; both or neither) the step's cache write
+ * is fused in at the plan's slots (none when the plan had no slot_mapping),
+ * bit-exact as mvk_reshape_and_cache. The summation order differs from the
+ * unplanned call's, so the two may differ in the last bits (both within the
+ * same bound of the exact result); planned calls with the same plan and inputs
+ * give identical bits.
+ *   out, q, k_cache, v_cache, scale, dtype, block_size: as for decode.
+ *   plan, plan_bytes: a plan built by mvk_paged_attention_plan (stream order).
+ * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED,
+ * MVK_ERR_WORKSPACE_TOO_SMALL (plan_bytes), MVK_ERR_HIP.
+ */
+int32_t mvk_paged_attention_decode_planned(void* out, const void* q, void* k_cache,
+                                           void* v_cache, const void* new_key,
+                                           const void* new_value, const void* plan,
+                                           size_t plan_bytes, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t max_context_len,
+                                           float scale, int32_t dtype, void* stream);
+
+/*
  * mvk_paged_attention_decode_noalloc - mvk_paged_attention_decode without a
  * workspace argument, for callers that cannot allocate device memory (code
  * under graph capture, tight serving loops, harnesses that forbid hipMalloc).

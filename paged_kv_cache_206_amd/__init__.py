@@ -13,6 +13,10 @@ is no fallback: if libmvk.so is missing, the first call fails with instructions.
                                    scale, max_context_len, out, partition_tokens=0,
                                    new_key=None, new_value=None, slot_mapping=None)
     workspace_size(...), workspace_bytes(...), scratch_limit()
+    plan_size(...), make_plan(block_tables, context_lens, num_q_heads, head_dim,
+                              max_context_len, slot_mapping=None, plan=None)
+    paged_attention_decode_planned(q, k_cache, v_cache, plan, scale, max_context_len,
+                                   out=None, new_key=None, new_value=None)
     paged_attention_multi_query(q, k_cache, v_cache, block_tables, context_lens,
                                 query_start, scale, max_query_len=None,
                                 max_context_len=None, out=None, partition_tokens=0,
@@ -68,6 +72,14 @@ SIGNATURES = {
                                                     _c_int, _c_int, _c_int, _c_float, _c_int,
                                                     _c_int, _ptr]),
     "mvk_paged_attention_scratch_limit": (_c_size, []),
+    "mvk_paged_attention_plan_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
+                                               ctypes.POINTER(_c_size)]),
+    "mvk_paged_attention_plan": (_c_int, [_ptr, _c_size, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _ptr]),
+    "mvk_paged_attention_decode_planned": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                                    _c_size, _c_int, _c_int, _c_int, _c_int,
+                                                    _c_int, _c_int, _c_int, _c_float, _c_int,
+                                                    _ptr]),
     "mvk_stream_read_probe": (_c_int, [_ptr, _c_size, _ptr, _c_int, _ptr]),
     "mvk_paged_attention_multi_query_workspace_size": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -328,6 +340,91 @@ def paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
         _stream(q, out, k_cache, v_cache, block_tables, context_lens, new_key, new_value,
                 slot_mapping))
     _check("mvk_paged_attention_decode_noalloc", st)
+    return out
+
+
+def plan_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+              max_context_len: int):
+    """Bytes of a decode plan for these sizes, or None when the planned path
+    does not cover them (paged_attention_decode covers every batch)."""
+    nbytes = ctypes.c_size_t(0)
+    st = lib().mvk_paged_attention_plan_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_context_len, ctypes.byref(nbytes))
+    if st == MVK_ERR_UNSUPPORTED:
+        return None
+    _check("mvk_paged_attention_plan_size", st)
+    return nbytes.value
+
+
+def make_plan(block_tables: torch.Tensor, context_lens: torch.Tensor, num_q_heads: int,
+              num_kv_heads: int, head_dim: int, max_context_len: int,
+              slot_mapping: torch.Tensor | None = None,
+              plan: torch.Tensor | None = None) -> torch.Tensor:
+    """Build a decode step's plan on the device (asynchronous on the current
+    stream) from its block tables, context lengths and, for fused cache
+    writes, its new-token slots; returns the plan (uint8 device tensor, a
+    snapshot of those arrays) for paged_attention_decode_planned."""
+    _require(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _require(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    S = context_lens.shape[0]
+    if block_tables.shape[0] != S:
+        raise ValueError("inconsistent shapes")
+    if slot_mapping is not None:
+        _require(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+        if slot_mapping.shape[0] != S:
+            raise ValueError("slot_mapping must have one slot per sequence")
+    need = plan_size(S, num_q_heads, num_kv_heads, head_dim, max_context_len)
+    if need is None:
+        raise MvkError("mvk_paged_attention_plan_size", MVK_ERR_UNSUPPORTED)
+    if plan is None:
+        plan = torch.empty(max(need, 16), dtype=torch.uint8, device=context_lens.device)
+    _require(plan, "plan", dtype=torch.uint8)
+    st = lib().mvk_paged_attention_plan(
+        plan.data_ptr(), plan.numel(), block_tables.data_ptr(), context_lens.data_ptr(),
+        None if slot_mapping is None else slot_mapping.data_ptr(), S, num_q_heads, num_kv_heads,
+        head_dim, block_tables.shape[1], max_context_len,
+        _stream(context_lens, block_tables, slot_mapping, plan))
+    _check("mvk_paged_attention_plan", st)
+    return plan
+
+
+def paged_attention_decode_planned(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   plan: torch.Tensor, scale: float, max_context_len: int,
+                                   out: torch.Tensor | None = None,
+                                   new_key: torch.Tensor | None = None,
+                                   new_value: torch.Tensor | None = None) -> torch.Tensor:
+    """One layer's decode step through a plan (make_plan): the result of
+    paged_attention_decode for the arrays the plan was built from; with
+    new_key / new_value the cache write is fused in at the plan's slots.
+    `max_context_len` must be the plan's."""
+    _require(q, "q", ndim=3)
+    _require(k_cache, "k_cache", dtype=q.dtype, ndim=4)
+    _require(v_cache, "v_cache", dtype=q.dtype, ndim=4)
+    _require(plan, "plan", dtype=torch.uint8)
+    S, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d:
+        raise ValueError("inconsistent shapes")
+    if (new_key is None) != (new_value is None):
+        raise ValueError("new_key and new_value go together")
+    if new_key is not None:
+        _require(new_key, "new_key", dtype=q.dtype, ndim=3)
+        _require(new_value, "new_value", dtype=q.dtype, ndim=3)
+        if new_key.shape != (S, hkv, d) or new_value.shape != new_key.shape:
+            raise ValueError("fused cache write: new rows must be [num_seqs, Hkv, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", dtype=q.dtype)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    st = lib().mvk_paged_attention_decode_planned(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        None if new_key is None else new_key.data_ptr(),
+        None if new_value is None else new_value.data_ptr(), plan.data_ptr(), plan.numel(), S, hq,
+        hkv, d, bs, nb, max_context_len, float(scale), _dtype_code(q),
+        _stream(q, out, k_cache, v_cache, plan, new_key, new_value))
+    _check("mvk_paged_attention_decode_planned", st)
     return out
 
 

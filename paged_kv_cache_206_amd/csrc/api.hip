@@ -223,6 +223,50 @@ int32_t check_mq_sizes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_q
 }
 
 
+// ------------------------------------------------ planned decode (plan once per step)
+
+// Bins (workgroups of mvk::kPlanWaves waves) of a decode plan: as many as the
+// chip runs at once (one per CU at head_dim 128 with g >= 2, whose kernel
+// holds two waves per SIMD; two per CU elsewhere, four waves per SIMD), more
+// when the items would not fit their waves, and no more than there are
+// (sequence, KV head) items. Contexts up to kPlanWaves * kPlanMaxBlocks
+// blocks (7168 tokens) are covered.
+constexpr int32_t kCus = 256;
+
+struct PlanGeom {
+  int32_t bins;
+  size_t bytes;
+};
+
+int32_t plan_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t max_context_len, PlanGeom* g) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_kv_heads > kMaxGridYZ ||
+      max_context_len < 0)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return MVK_ERR_INVALID_ARGUMENT;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!mvk::decode_supported(head_dim, group)) return MVK_ERR_UNSUPPORTED;
+  if (num_seqs > mvk::kPlanMaxSeqs) return MVK_ERR_UNSUPPORTED;
+  const int64_t items = (int64_t)num_seqs * num_kv_heads;
+  const int32_t waves_per_simd = (head_dim == 64 || group == 1) ? 4 : 2;
+  const int64_t cap = (int64_t)kCus * (4 * waves_per_simd / mvk::kPlanWaves);
+  // an item needs a wave per kPlanMaxBlocks blocks, so a bin holds at most
+  // kPlanWaves / that many items; batches with more items than the resident
+  // bins hold take more bins (a second round of workgroups)
+  const int64_t blocks = ((int64_t)max_context_len + kBlock - 1) / kBlock;
+  int64_t waves_per_item = (blocks + mvk::kPlanMaxBlocks - 1) / mvk::kPlanMaxBlocks;
+  if (waves_per_item < 1) waves_per_item = 1;
+  if (waves_per_item > mvk::kPlanWaves) return MVK_ERR_UNSUPPORTED;
+  const int64_t items_per_bin = mvk::kPlanWaves / waves_per_item;
+  int64_t bins = (items + items_per_bin - 1) / items_per_bin;
+  if (bins < cap) bins = cap;
+  if (bins > items) bins = items;
+  if (bins > INT32_MAX / (mvk::kPlanWaves * mvk::kPlanDescInts)) return MVK_ERR_UNSUPPORTED;
+  g->bins = (int32_t)bins;
+  g->bytes = (size_t)bins * mvk::kPlanWaves * mvk::kPlanDescInts * 4u;
+  return MVK_OK;
+}
+
 // ------------------------------------------- static scratch (allocation-free calls)
 // The allocation-free decode entry point keeps its partial states, partition
 // counters and work list in this array instead of a caller workspace. Every
@@ -436,6 +480,98 @@ int32_t mvk_paged_attention_decode(void* out, const void* q, void* k_cache, void
                      slot_mapping, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
                      partition_tokens, workspace, workspace_bytes, (hipStream_t)stream, false);
+}
+
+int32_t mvk_paged_attention_plan_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len, size_t* plan_bytes) {
+  if (!plan_bytes) return MVK_ERR_INVALID_ARGUMENT;
+  PlanGeom g{};
+  const int32_t st =
+      plan_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, &g);
+  if (st != MVK_OK) return st;
+  *plan_bytes = g.bytes;
+  return MVK_OK;
+}
+
+int32_t mvk_paged_attention_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* slot_mapping,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq,
+                                 int32_t max_context_len, void* stream) {
+  PlanGeom g{};
+  const int32_t st =
+      plan_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, &g);
+  if (st != MVK_OK) return st;
+  if (max_blocks_per_seq <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (g.bins == 0) return MVK_OK;
+  if (!plan || !block_tables || !context_lens) return MVK_ERR_INVALID_ARGUMENT;
+  if (!aligned16(plan) || !aligned4(block_tables) || !aligned4(context_lens) ||
+      (slot_mapping && !aligned4(slot_mapping)))
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (plan_bytes < g.bytes) return MVK_ERR_WORKSPACE_TOO_SMALL;
+  mvk::DecodePlanArgs a{};
+  a.plan = (int32_t*)plan;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.slot_mapping = slot_mapping;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_bins = g.bins;
+  const hipError_t err = mvk::launch_decode_plan(a, (hipStream_t)stream);
+  return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
+}
+
+int32_t mvk_paged_attention_decode_planned(void* out, const void* q, void* k_cache,
+                                           void* v_cache, const void* new_key,
+                                           const void* new_value, const void* plan,
+                                           size_t plan_bytes, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t max_context_len,
+                                           float scale, int32_t dtype, void* stream) {
+  if (dtype != MVK_F16 && dtype != MVK_BF16) return MVK_ERR_INVALID_ARGUMENT;
+  if (block_size != kBlock) return MVK_ERR_UNSUPPORTED;
+  if (num_blocks <= 0 || !isfinite(scale)) return MVK_ERR_INVALID_ARGUMENT;
+  PlanGeom g{};
+  const int32_t st =
+      plan_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, &g);
+  if (st != MVK_OK) return st;
+  if (g.bins == 0) return MVK_OK;
+  if (!out || !q || !k_cache || !v_cache || !plan) return MVK_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(plan))
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (out == q || out == k_cache || out == v_cache || k_cache == v_cache)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (plan_bytes < g.bytes) return MVK_ERR_WORKSPACE_TOO_SMALL;
+  if (new_key || new_value) {  // fused cache write at the plan's slots: both rows or none
+    if (!new_key || !new_value || !aligned16(new_key) || !aligned16(new_value))
+      return MVK_ERR_INVALID_ARGUMENT;
+    if ((int64_t)num_blocks * kBlock > INT32_MAX) return MVK_ERR_INVALID_ARGUMENT;
+  }
+  mvk::PlannedDecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.new_key = new_key;
+  a.new_value = new_value;
+  a.plan = (const int32_t*)plan;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.num_bins = g.bins;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  a.dtype = dtype;
+  const hipError_t err = mvk::launch_paged_decode_planned(a, (hipStream_t)stream);
+  return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
 }
 
 int32_t mvk_paged_attention_decode_noalloc(void* out, const void* q, void* k_cache,

@@ -76,6 +76,8 @@ struct MfmaPolicy {
   };
 
   uint4 qop[NKS];
+  uint4 nk_ov[NKS];  // the step's new K row pieces of this lane (load_new_row)
+  VT nv_ov;          // and its new V row piece
   f32x4_t acc[NE];
   float m, lsum;
   int r16, q4;
@@ -151,6 +153,36 @@ struct MfmaPolicy {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (4 * q4 + i == row_new) f.v[i] = ((const VT*)nv)[r16];
+      }
+    }
+    step(f, tok0, r16 < G ? t_end : 0, scale_log2);
+  }
+
+  // The step's new K/V row (nk_row / nv_row: this KV head's D elements),
+  // loaded straight into the operand layout by the lanes that hold the new
+  // token's K row (row slot row_new) and its V quarter; process_own then
+  // takes them in place of the pool's row. No LDS and no barrier: only the
+  // wave whose blocks include the new slot calls it.
+  __device__ __forceinline__ void load_new_row(const uint16_t* nk_row, const uint16_t* nv_row) {
+    if (r16 == row_new) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) nk_ov[ks] = *(const uint4*)(nk_row + 8 * (4 * ks + q4));
+    }
+    if (q4 == (row_new >> 2)) nv_ov = *(const VT*)(nv_row + VW * r16);
+  }
+
+  // As process, with the new row from load_new_row's registers.
+  __device__ __forceinline__ void process_own(Frag& f, int tok0, int t_end, float scale_log2,
+                                              bool sub) {
+    arrange(f);
+    if (sub) {
+      if (r16 == row_new) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) f.k[ks] = nk_ov[ks];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * q4 + i == row_new) f.v[i] = nv_ov;
       }
     }
     step(f, tok0, r16 < G ? t_end : 0, scale_log2);

@@ -117,6 +117,16 @@ __device__ __forceinline__ float collect(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workgroup barrier that orders LDS only: each wave's LDS writes complete
+// before the barrier and are visible to every wave after it, while its
+// global loads and stores stay in flight (a full __syncthreads also waits
+// for them, which puts a memory round trip before the code that follows).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Cross-lane moves inside a 16-lane DPP row.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {

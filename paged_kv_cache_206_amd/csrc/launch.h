@@ -59,6 +59,40 @@ bool decode_supported(int32_t head_dim, int32_t group);
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Planned single-pass decode: a plan built once per decode step (block
+// tables, lengths and new-token slots of the step) that every layer's call
+// reads. The plan is num_bins * kPlanWaves descriptors of kPlanDescInts ints.
+constexpr int32_t kPlanWaves = 8;        // waves per bin (workgroup)
+constexpr int32_t kPlanDescInts = 64;    // ints per wave descriptor
+constexpr int32_t kPlanHdrInts = 8;      // descriptor header; the rest are block ids
+constexpr int32_t kPlanMaxBlocks = kPlanDescInts - kPlanHdrInts;  // blocks per wave
+constexpr int32_t kPlanMaxSeqs = 1024;   // sequences one plan ranks (in LDS)
+
+struct DecodePlanArgs {
+  int32_t* plan;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* slot_mapping;  // nullptr: no new-token slots recorded
+  int32_t num_seqs, num_kv_heads, max_blocks_per_seq, max_context_len, num_bins;
+};
+
+hipError_t launch_decode_plan(const DecodePlanArgs& a, hipStream_t stream);
+
+struct PlannedDecodeArgs {
+  void* out;
+  const void* q;
+  void* k_cache;
+  void* v_cache;
+  const void* new_key;    // fused cache write (nullptr = none), at the plan's slots
+  const void* new_value;
+  const int32_t* plan;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_context_len, num_bins;
+  float scale_log2;
+  int32_t dtype;
+};
+
+hipError_t launch_paged_decode_planned(const PlannedDecodeArgs& a, hipStream_t stream);
+
 struct MultiQueryArgs {
   void* out;                   // [T, Hq, D]
   const void* q;               // [T, Hq, D]

@@ -1,0 +1,439 @@
+// Planned paged-attention decode for gfx950 (CDNA4), wave64: the work of a
+// decode step is laid out once per step (a plan), and every layer's decode
+// call of that step reads it.
+//
+// Method (mini-vllm write-up, "2. 分页KV缓存（PagedAttention）" and
+// "关键工程决策" items 1-3): every running sequence's single new query token
+// attends over its cached context, read block by block through its block
+// table; in steady state all running sequences form one batched decode step,
+// and every layer of the model runs that same step over its own pools with
+// the same block tables and lengths. The plan exploits exactly that: the
+// tables and lengths are read, ranked and dealt out once per step instead of
+// once per layer.
+//
+// Work decomposition (single pass: every (sequence, KV head) item is done by
+// one workgroup, so no partial state leaves the workgroup):
+//  * The plan kernel ranks the sequences by block count (longest first, ties
+//    by index) and deals the items (rank-major, KV head fastest) to B bins
+//    in boustrophedon rounds: round k gives item k*B + p to bin p on even
+//    rounds and to bin B-1-p on odd ones, so each bin pairs long items with
+//    short ones and all bins carry about the same number of blocks.
+//  * A bin is one workgroup of W waves. Its waves are split over its items
+//    to keep the largest number of blocks any wave streams small (greedy:
+//    each item gets the waves its descriptors need, then every spare wave
+//    goes to the item whose waves carry the most blocks each), and each wave
+//    takes a contiguous run of its item's blocks.
+//  * Each wave's work is one 64-int descriptor: sequence, KV head, token
+//    range, the sequence's new-token slot and context length, its item's
+//    wave range, and the physical ids of its blocks (copied from the block
+//    table). The decode kernel's wave fetches it with one load, so K/V loads
+//    start after a single round trip, and no wave ranks or searches anything.
+//  * The waves of an item merge their online-softmax states through LDS
+//    (log-sum-exp rule, fixed order) and write the item's rows.
+// Per-block compute is the MFMA tile (g >= 2) or the VALU policy (g = 1).
+// Fused cache write without any barrier: the wave whose blocks include the
+// sequence's new slot loads the step's new K/V row straight into the operand
+// layout and uses it in place of the pool's row, and the item's first wave
+// stores the row into the pools (the store of record). A sequence appends
+// only into its own blocks, which no other sequence reads (the paged
+// allocator's rule), so no other item waits for that store.
+#include <type_traits>
+
+#include "attention_mfma.h"
+#include "attention_valu.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace mvk {
+
+namespace {
+
+// Descriptor fields (ints 0..7); ints 8..63 are block ids.
+enum : int {
+  kDescSeq = 0,       // sequence (negative: idle wave)
+  kDescHead = 1,      // KV head
+  kDescTokBegin = 2,  // first token of the wave's run (a multiple of 16)
+  kDescTokEnd = 3,    // one past its last token
+  kDescSlot = 4,      // the sequence's new-token slot (fused cache write), or -1
+  kDescWaves = 5,     // first wave of the item (bits 0-7), waves of the item (bits 8-15)
+  kDescLen = 6,       // the sequence's context length
+};
+
+constexpr int kBinThreads = 256;
+
+template <int D, int G>
+constexpr int kPlannedWavesPerSimd = (D == 64 || G == 1) ? 4 : 2;
+
+struct PlannedShape {
+  int32_t num_seqs, num_kv_heads, num_blocks, max_context_len;
+  float scale_log2;
+};
+
+// Merge of the N waves wb .. wb+N-1 of an item (N known at compile time, so
+// only their LDS slots are read and every loop unrolls): element (j, d) of
+// the item's g x D outputs is sum_w o_w 2^(m_w - M) / sum_w l_w 2^(m_w - M),
+// waves in order, M their largest reference; the division is one reciprocal
+// of the denominator (the output is rounded to 16 bits).
+template <int N, int W, int G, int D, int DT>
+__device__ __forceinline__ void merge_item(uint16_t* __restrict__ out, const float (*sm_o)[G * D],
+                                           const float (*sm_m)[G], const float (*sm_l)[G], int wb,
+                                           int wave, int lane, int s, int h, int Hq) {
+  using E = Elem<DT>;
+  for (int idx = (wave - wb) * 64 + lane; idx < G * D; idx += N * 64) {
+    const int j = idx / D;
+    float m[N], l[N], o[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      m[n] = sm_m[wb + n][j];
+      l[n] = sm_l[wb + n][j];
+      o[n] = sm_o[wb + n][idx];
+    }
+    float mm = m[0];
+#pragma unroll
+    for (int n = 1; n < N; ++n) mm = fmaxf(mm, m[n]);
+    float lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const float fct = fast_exp2(m[n] - mm);
+      lsum = fmaf(l[n], fct, lsum);
+      acc = fmaf(o[n], fct, acc);
+    }
+    out[((size_t)s * Hq + (size_t)h * G) * D + idx] =
+        E::round(lsum > 0.0f ? acc * __builtin_amdgcn_rcpf(lsum) : 0.0f);
+  }
+}
+
+template <int DT, int D, int G, int W, int NPF, bool USE_MFMA, bool FUSED>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
+    kPlannedWavesPerSimd<D, G>))) void paged_decode_planned_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, const int32_t* __restrict__ plan, PlannedShape sh,
+    const uint16_t* __restrict__ new_key, const uint16_t* __restrict__ new_value) {
+  using Policy =
+      typename std::conditional<USE_MFMA, MfmaPolicy<DT, D, G>, ValuPolicy<DT, D, G>>::type;
+  __shared__ float sm_o[W][G * D];
+  __shared__ float sm_m[W][G];
+  __shared__ float sm_l[W][G];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  // lane k holds descriptor int k
+  const int dv = plan[((size_t)blockIdx.x * W + wave) * kPlanDescInts + lane];
+  const int s_raw = __builtin_amdgcn_readlane(dv, kDescSeq);
+  const int h_raw = __builtin_amdgcn_readlane(dv, kDescHead);
+  // every field is clamped into range, so an inconsistent plan gives wrong
+  // rows but no access outside the buffers
+  const bool active = s_raw >= 0 && s_raw < sh.num_seqs && h_raw >= 0 && h_raw < sh.num_kv_heads;
+  const int s = active ? s_raw : 0;
+  const int h = active ? h_raw : 0;
+  const int L = min(max(__builtin_amdgcn_readlane(dv, kDescLen), 0), sh.max_context_len);
+  const int tb = min(max(__builtin_amdgcn_readlane(dv, kDescTokBegin), 0), L) & ~(kBlockTokens - 1);
+  const int te = min(max(__builtin_amdgcn_readlane(dv, kDescTokEnd), tb), L);
+  const int nblk = active ? min((te - tb + kBlockTokens - 1) / kBlockTokens, kPlanMaxBlocks) : 0;
+  const int wv = __builtin_amdgcn_readlane(dv, kDescWaves);
+  const int wb = min(wv & 0xff, W - 1);
+  const int wn = min(max((wv >> 8) & 0xff, 1), W - wb);
+  const bool in_item = active && wave >= wb && wave < wb + wn;
+
+  const int Hq = sh.num_kv_heads * G;
+  const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;
+  const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
+  Policy pol;
+  int slot = -1;
+  if constexpr (FUSED) slot = __builtin_amdgcn_readlane(dv, kDescSlot);
+  const bool has_new = FUSED && in_item && slot >= 0 && slot < sh.num_blocks * kBlockTokens;
+  const int blk_new = has_new ? slot / kBlockTokens : -1;
+  if constexpr (FUSED) pol.row_new = has_new ? slot % kBlockTokens : -1;
+  const bool writer = has_new && wave == wb;  // the store of record: the item's first wave
+  // the wave whose blocks include the new slot's block reads the new row in
+  // place of the pool's
+  const bool holder =
+      has_new && __ballot(lane >= kPlanHdrInts && lane < kPlanHdrInts + nblk && dv == blk_new) != 0;
+  uint4 nk16 = make_uint4(0u, 0u, 0u, 0u), nv16 = nk16;
+
+  const char* kbase = (const char*)(k_cache + (size_t)h * D);
+  const char* vbase = (const char*)(v_cache + (size_t)h * D);
+  typename Policy::Frag f[NPF];
+  auto block_of = [&](int k) {
+    const int blk = __builtin_amdgcn_readlane(dv, kPlanHdrInts + min(k, nblk - 1));
+    return ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
+  };
+  // Rows of block k that hold context tokens are read through its buffer
+  // descriptor; rows past te read as zero, and steps past the last block
+  // load through an empty descriptor (zeros, no memory access).
+  auto load_block = [&](typename Policy::Frag& fr, int k) {
+    const bool real = k < nblk;
+    const int blk = block_of(k);
+    const int kk = min(k, nblk - 1);
+    const int rows = min(kBlockTokens, te - (tb + kk * kBlockTokens));
+    const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
+    const size_t o = (size_t)blk * block_bytes;
+    pol.template load<kStreamLoad>(fr, make_rsrc(kbase + o, extent), make_rsrc(vbase + o, extent),
+                                   row_bytes);
+  };
+
+  if (in_item) {
+    pol.init(q, (size_t)s * Hq + (size_t)h * G, lane, row_bytes);
+    if constexpr (FUSED) {
+      const size_t src = ((size_t)s * sh.num_kv_heads + h) * D;
+      if (writer && lane < D / 8) {
+        nk16 = *(const uint4*)(new_key + src + lane * 8);
+        nv16 = *(const uint4*)(new_value + src + lane * 8);
+      }
+      if (holder) pol.load_new_row(new_key + src, new_value + src);
+    }
+    // Loads complete in issue order: the query and new-row loads go out
+    // before the K/V stream, so the first block is computed as soon as it
+    // lands instead of after the blocks issued ahead of a late query load.
+    __builtin_amdgcn_sched_barrier(0);
+    if (nblk > 0) {
+#pragma unroll
+      for (int j = 0; j < NPF - 1; ++j) load_block(f[j], j);
+      for (int k0 = 0;; k0 += NPF) {
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+          const int k = k0 + j;
+          load_block(f[(j + NPF - 1) % NPF], k + NPF - 1);
+          pol.process_own(f[j], tb + k * kBlockTokens, te, sh.scale_log2,
+                          holder && block_of(k) == blk_new);
+          if (k + 1 >= nblk) goto blocks_done;
+        }
+      }
+    blocks_done:;
+    }
+    if constexpr (FUSED) {
+      // the store of record (after the blocks: storing earlier would make
+      // this wave wait for the new row before issuing its next K/V loads)
+      if (writer && lane < D / 8) {
+        const size_t dst = (size_t)slot * sh.num_kv_heads * D + (size_t)h * D + lane * 8;
+        *(uint4*)(k_cache + dst) = nk16;
+        *(uint4*)(v_cache + dst) = nv16;
+      }
+    }
+  }
+  if (in_item) pol.to_lds(sm_m[wave], sm_l[wave], sm_o[wave]);
+  lds_barrier();  // the writer's pool stores and any other global traffic stay in flight
+  if (!in_item) return;
+
+  // The item's waves merge their states (log-sum-exp rule, waves in order)
+  // and write its g output rows; an empty context gives zeros.
+  switch (wn) {
+    case 1: merge_item<1, W, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, s, h, Hq); break;
+    case 2: merge_item<2, W, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, s, h, Hq); break;
+    case 3: merge_item<3, W, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, s, h, Hq); break;
+    case 4: merge_item<4, W, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, s, h, Hq); break;
+    case 5: merge_item<5, W, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, s, h, Hq); break;
+    case 6: merge_item<6, W, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, s, h, Hq); break;
+    case 7: merge_item<7, W, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, s, h, Hq); break;
+    default: merge_item<8, W, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, s, h, Hq); break;
+  }
+}
+
+// One workgroup per bin. Every workgroup ranks the whole batch in LDS (at
+// most kPlanMaxSeqs sequences), assembles its own bin and writes its W
+// descriptors; workgroups do not communicate.
+struct BinShape {
+  int32_t num_seqs, num_kv_heads, max_blocks, max_context_len, num_bins;
+};
+
+template <int W>
+__global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
+    int32_t* __restrict__ plan, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ slots, BinShape ps) {
+  __shared__ int32_t nblk[kPlanMaxSeqs];
+  __shared__ int32_t lens[kPlanMaxSeqs];
+  __shared__ int32_t slot_of[kPlanMaxSeqs];
+  __shared__ __attribute__((aligned(16))) int32_t keys[kPlanMaxSeqs];
+  __shared__ int32_t rank_of[kPlanMaxSeqs];
+  __shared__ int32_t seq_of_rank[kPlanMaxSeqs];
+  __shared__ int32_t hdr[W][kPlanHdrInts];
+  const int t = threadIdx.x;
+  const int S = ps.num_seqs;
+  const int S4 = (S + 3) & ~3;
+  for (int s = t; s < S4; s += kBinThreads) {
+    int key = -1;  // padding: never larger than a real key
+    if (s < S) {
+      const int L = min(max(context_lens[s], 0), ps.max_context_len);
+      const int nb = (L + kBlockTokens - 1) / kBlockTokens;
+      lens[s] = L;
+      nblk[s] = nb;
+      slot_of[s] = slots != nullptr ? slots[s] : -1;
+      rank_of[s] = 0;
+      // unique key, larger = earlier: more blocks first, then lower index
+      key = (nb << 10) | (kPlanMaxSeqs - 1 - s);
+    }
+    keys[s] = key;
+  }
+  __syncthreads();
+  // rank = number of larger keys (a permutation of 0..S-1). Sequence s gets
+  // P = 256 / S threads (at least one), each counting over its slice of the
+  // keys four at a time; the slices' counts meet in LDS.
+  {
+    const int P = S <= kBinThreads ? kBinThreads / S : 1;
+    const int chunks = S4 / 4;
+    const int per = (chunks + P - 1) / P;  // 4-key chunks per slice
+    for (int w = t; w < S * P; w += kBinThreads) {
+      const int s = w / P, p = w % P;
+      const int mine = keys[s];
+      const int c1 = min(chunks, (p + 1) * per);
+      int cnt = 0;
+      for (int c = p * per; c < c1; ++c) {
+        const int4 k4 = *(const int4*)(keys + 4 * c);
+        cnt += (k4.x > mine) + (k4.y > mine) + (k4.z > mine) + (k4.w > mine);
+      }
+      if (cnt) atomicAdd(&rank_of[s], cnt);
+    }
+  }
+  __syncthreads();
+  for (int s = t; s < S; s += kBinThreads) seq_of_rank[rank_of[s]] = s;
+  __syncthreads();
+  if (t < W) {
+    // Every one of the first W threads assembles the bin (the same answer,
+    // in registers, with loops over the W possible item slots) and writes
+    // the header of wave t. Item slot k is round k's item, present when that
+    // round reaches this bin.
+    const int N = S * ps.num_kv_heads;
+    const int B = ps.num_bins;
+    const int b = blockIdx.x;
+    int is[W], ih[W], inb[W], iw[W];
+    int used = 0;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      const int i = k * B + ((k & 1) ? B - 1 - b : b);
+      const bool ok = k * B < N && i < N;
+      const int s = ok ? seq_of_rank[i / ps.num_kv_heads] : 0;
+      is[k] = s;
+      ih[k] = ok ? i % ps.num_kv_heads : 0;
+      inb[k] = ok ? nblk[s] : 0;
+      // every item gets the waves its descriptors need (at least one)
+      iw[k] = ok ? max(1, (inb[k] + kPlanMaxBlocks - 1) / kPlanMaxBlocks) : 0;
+      used += iw[k];
+    }
+    // each spare wave goes to the item whose waves carry the most blocks
+    // (largest blocks / waves, compared by cross-multiplication; the first
+    // such item on ties)
+    for (; used < W; ++used) {
+      int best = 0;
+#pragma unroll
+      for (int k = 1; k < W; ++k) {
+        if (iw[k] > 0 && (iw[best] == 0 || inb[k] * iw[best] > inb[best] * iw[k])) best = k;
+      }
+#pragma unroll
+      for (int k = 0; k < W; ++k) iw[k] += (k == best) ? 1 : 0;
+    }
+    // wave t's item: items take consecutive waves in slot order
+    int wb = 0, item = -1;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      const bool mine = item < 0 && iw[k] > 0 && t < wb + iw[k];
+      if (mine) item = k;
+      if (item < 0) wb += iw[k];
+    }
+    int* hw = hdr[t];
+    if (item < 0) {
+#pragma unroll
+      for (int k = 0; k < kPlanHdrInts; ++k) hw[k] = 0;
+      hw[kDescSeq] = -1;
+    } else {
+      int s = 0, h = 0, nb = 0, wn = 0;
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        if (k == item) {
+          s = is[k];
+          h = ih[k];
+          nb = inb[k];
+          wn = iw[k];
+        }
+      }
+      const int x = t - wb;
+      const int b0 = x * nb / wn, b1 = (x + 1) * nb / wn;
+      hw[kDescSeq] = s;
+      hw[kDescHead] = h;
+      hw[kDescTokBegin] = b0 * kBlockTokens;
+      hw[kDescTokEnd] = min(b1 * kBlockTokens, lens[s]);
+      hw[kDescSlot] = slot_of[s];
+      hw[kDescWaves] = wb | (wn << 8);
+      hw[kDescLen] = lens[s];
+      hw[7] = 0;
+    }
+  }
+  __syncthreads();
+  for (int idx = t; idx < W * kPlanDescInts; idx += kBinThreads) {
+    const int w = idx / kPlanDescInts;
+    const int k = idx % kPlanDescInts;
+    int v;
+    if (k < kPlanHdrInts) {
+      v = hdr[w][k];
+    } else {
+      const int s = hdr[w][kDescSeq];
+      const int tb = hdr[w][kDescTokBegin];
+      const int n = s >= 0 ? max(hdr[w][kDescTokEnd] - tb + kBlockTokens - 1, 0) / kBlockTokens : 0;
+      const int j = k - kPlanHdrInts;
+      v = j < n ? block_tables[(size_t)s * ps.max_blocks + tb / kBlockTokens + j] : -1;
+    }
+    plan[((size_t)blockIdx.x * W + w) * kPlanDescInts + k] = v;
+  }
+}
+
+template <int DT, int D, int G, int W, int NPF, bool MFMA>
+hipError_t launch_planned_typed(const PlannedDecodeArgs& a, hipStream_t stream) {
+  PlannedShape sh{a.num_seqs, a.num_kv_heads, a.num_blocks, a.max_context_len, a.scale_log2};
+  if (a.new_key != nullptr) {
+    hipLaunchKernelGGL((paged_decode_planned_kernel<DT, D, G, W, NPF, MFMA, true>),
+                       dim3((unsigned)a.num_bins), dim3(W * 64), 0, stream, (uint16_t*)a.out,
+                       (const uint16_t*)a.q, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache, a.plan, sh,
+                       (const uint16_t*)a.new_key, (const uint16_t*)a.new_value);
+  } else {
+    hipLaunchKernelGGL((paged_decode_planned_kernel<DT, D, G, W, NPF, MFMA, false>),
+                       dim3((unsigned)a.num_bins), dim3(W * 64), 0, stream, (uint16_t*)a.out,
+                       (const uint16_t*)a.q, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache, a.plan, sh,
+                       nullptr, nullptr);
+  }
+  return hipGetLastError();
+}
+
+// Blocks in flight per wave: three where the MFMA tile at head_dim 128 leaves
+// room under the two-waves-per-SIMD register budget (a plan of short
+// contexts gives each wave at most three blocks, all then in flight at
+// once), two elsewhere (four waves per SIMD need <= 128 VGPRs).
+template <int D, int G>
+constexpr int kPlannedPrefetch = (D == 128 && G >= 2) ? 3 : 2;
+
+template <int DT, int D, int G>
+hipError_t launch_planned_group(const PlannedDecodeArgs& a, hipStream_t stream) {
+  constexpr bool kMfma = G >= 2;
+  return launch_planned_typed<DT, D, G, kPlanWaves, kPlannedPrefetch<D, G>, kMfma>(a, stream);
+}
+
+template <int DT, int D>
+hipError_t launch_planned_dim(const PlannedDecodeArgs& a, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_planned_group<DT, D, 1>(a, stream);
+    case 2: return launch_planned_group<DT, D, 2>(a, stream);
+    case 4: return launch_planned_group<DT, D, 4>(a, stream);
+    case 8: return launch_planned_group<DT, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_plan(const DecodePlanArgs& a, hipStream_t stream) {
+  BinShape ps{a.num_seqs, a.num_kv_heads, a.max_blocks_per_seq, a.max_context_len, a.num_bins};
+  hipLaunchKernelGGL((paged_decode_plan_bins_kernel<kPlanWaves>), dim3((unsigned)a.num_bins),
+                     dim3(kBinThreads), 0, stream, a.plan, a.block_tables, a.context_lens,
+                     a.slot_mapping, ps);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_decode_planned(const PlannedDecodeArgs& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  if (a.dtype == 0) {
+    return a.head_dim == 64 ? launch_planned_dim<0, 64>(a, group, stream)
+                            : launch_planned_dim<0, 128>(a, group, stream);
+  }
+  return a.head_dim == 64 ? launch_planned_dim<1, 64>(a, group, stream)
+                          : launch_planned_dim<1, 128>(a, group, stream);
+}
+
+}  // namespace mvk

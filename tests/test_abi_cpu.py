@@ -33,6 +33,8 @@ def test_header_declares_the_boundary():
         "mvk_paged_attention_workspace_size", "mvk_paged_attention_workspace_bytes",
         "mvk_paged_attention_decode", "mvk_paged_attention_decode_noalloc",
         "mvk_paged_attention_scratch_limit", "mvk_stream_read_probe",
+        "mvk_paged_attention_plan_size", "mvk_paged_attention_plan",
+        "mvk_paged_attention_decode_planned",
         "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query",
         "mvk_prefill_attention",
         "mvk_bm_create", "mvk_bm_destroy", "mvk_bm_num_free", "mvk_bm_can_admit", "mvk_bm_admit",
@@ -202,6 +204,76 @@ def test_workspace_bytes_bounds_every_kv_head_count(mvk):
         mvk.workspace_bytes(4, 4, 96, 45)
     with pytest.raises(mvk.MvkError):
         mvk.workspace_bytes(-1, 4, 64, 45)
+
+
+def test_plan_scope_and_size(mvk):
+    """The planned path covers single-pass batches: one bin per CU (256) of 8
+    waves at head_dim 128 with g >= 2, two per CU elsewhere, more when the
+    items would not fit their waves, never more bins than (sequence, KV head)
+    items; 64 ints per wave. Contexts over 7168 tokens and more than 1024
+    sequences are outside it."""
+    assert mvk.plan_size(60, 16, 8, 128, 256) == 256 * 8 * 64 * 4        # Qwen3 shape
+    assert mvk.plan_size(256, 32, 4, 64, 2048) == 512 * 8 * 64 * 4       # TinyLlama shape
+    assert mvk.plan_size(4, 4, 2, 64, 45) == 8 * 8 * 64 * 4              # tiny: one bin per item
+    assert mvk.plan_size(0, 4, 2, 64, 45) == 0
+    assert mvk.plan_size(32, 32, 8, 128, 32768) is None                  # Llama-7B long
+    assert mvk.plan_size(512, 16, 8, 128, 131072) is None                # skewed
+    assert mvk.plan_size(1025, 4, 2, 64, 45) is None
+    # more items than the resident bins hold: 8 items per bin, 257 bins
+    assert mvk.plan_size(257, 16, 8, 128, 300) == 257 * 8 * 64 * 4
+    # items needing three waves (up to 168 blocks): two items per bin
+    assert mvk.plan_size(300, 8, 8, 128, 2600) == 1200 * 8 * 64 * 4
+    assert mvk.plan_size(4, 4, 2, 64, 7168) == 8 * 8 * 64 * 4
+    assert mvk.plan_size(4, 4, 2, 64, 7169) is None
+    with pytest.raises(mvk.MvkError):
+        mvk.plan_size(4, 6, 4, 64, 45)
+
+
+def plan_call(mvk, **over):
+    a = dict(plan=FAKE * 9, pb=1 << 20, bt=FAKE * 5, cl=FAKE * 6, sm=None, S=4, hq=4, hkv=2, d=64,
+             mb=4, maxlen=45, stream=None)
+    a.update(over)
+    return mvk.lib().mvk_paged_attention_plan(a["plan"], a["pb"], a["bt"], a["cl"], a["sm"],
+                                             a["S"], a["hq"], a["hkv"], a["d"], a["mb"],
+                                             a["maxlen"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(plan=None), 1), (dict(bt=None), 1), (dict(cl=FAKE * 6 + 2), 1),
+    (dict(sm=FAKE * 7 + 1), 1), (dict(plan=FAKE * 9 + 4), 1), (dict(pb=100), 3),
+    (dict(maxlen=65), 1), (dict(mb=0), 1), (dict(d=96), 2), (dict(hq=6, hkv=4), 1),
+    (dict(S=2000), 2), (dict(maxlen=32768, mb=2048), 2), (dict(maxlen=7200, mb=500), 2),
+])
+def test_plan_validation(mvk, over, status):
+    assert plan_call(mvk, **over) == status
+
+
+def test_plan_empty_batch_is_noop(mvk):
+    assert plan_call(mvk, S=0, plan=None, bt=None, cl=None) == 0
+
+
+def planned_call(mvk, **over):
+    a = dict(out=FAKE, q=FAKE * 2, k=FAKE * 3, v=FAKE * 4, nk=None, nv=None, plan=FAKE * 9,
+             pb=1 << 20, S=4, hq=4, hkv=2, d=64, bs=16, nb=32, maxlen=45, scale=0.125, dtype=0,
+             stream=None)
+    a.update(over)
+    return mvk.lib().mvk_paged_attention_decode_planned(
+        a["out"], a["q"], a["k"], a["v"], a["nk"], a["nv"], a["plan"], a["pb"], a["S"], a["hq"],
+        a["hkv"], a["d"], a["bs"], a["nb"], a["maxlen"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=3), 1), (dict(bs=8), 2), (dict(nb=0), 1), (dict(scale=math.inf), 1),
+    (dict(plan=None), 1), (dict(q=None), 1), (dict(out=FAKE * 2), 1), (dict(v=FAKE * 3), 1),
+    (dict(pb=1000), 3), (dict(nk=FAKE * 8), 1), (dict(nk=FAKE * 8 + 2, nv=FAKE * 10), 1),
+    (dict(d=256), 2), (dict(S=4000), 2), (dict(maxlen=40000), 2), (dict(maxlen=7200), 2),
+])
+def test_planned_decode_validation(mvk, over, status):
+    assert planned_call(mvk, **over) == status
+
+
+def test_planned_decode_empty_batch_is_noop(mvk):
+    assert planned_call(mvk, S=0, out=None, q=None, plan=None) == 0
 
 
 def test_library_partition_choice(mvk):
