@@ -158,33 +158,66 @@ struct MfmaPolicy {
     step(f, tok0, r16 < G ? t_end : 0, scale_log2);
   }
 
-  // The step's new K/V row (nk_row / nv_row: this KV head's D elements),
-  // loaded straight into the operand layout by the lanes that hold the new
-  // token's K row (row slot row_new) and its V quarter; process_own then
-  // takes them in place of the pool's row. No LDS and no barrier: only the
-  // wave whose blocks include the new slot calls it.
+  // The step's new K/V row of this KV head (nk_row / nv_row: its D elements)
+  // for the planned kernel, which takes the new token before the blocks
+  // (seed_row) and stores the row (store_new_row) instead of taking it in
+  // place of a pool row: every lane loads the K pieces of its quarter
+  // (elements 32*ks + 8*q4 .. +7, the layout of its query operand) and the
+  // V piece of its columns (VW*r16 .. +VW-1, the layout of its accumulators).
   __device__ __forceinline__ void load_new_row(const uint16_t* nk_row, const uint16_t* nv_row) {
-    if (r16 == row_new) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) nk_ov[ks] = *(const uint4*)(nk_row + 8 * (4 * ks + q4));
-    }
-    if (q4 == (row_new >> 2)) nv_ov = *(const VT*)(nv_row + VW * r16);
+    for (int ks = 0; ks < NKS; ++ks) nk_ov[ks] = *(const uint4*)(nk_row + 32 * ks + 8 * q4);
+    nv_ov = *(const VT*)(nv_row + VW * r16);
   }
 
-  // As process, with the new row from load_new_row's registers.
-  __device__ __forceinline__ void process_own(Frag& f, int tok0, int t_end, float scale_log2,
-                                              bool sub) {
-    arrange(f);
-    if (sub) {
-      if (r16 == row_new) {
+  // Store the row loaded by load_new_row: lanes of row slot 0 write K,
+  // lanes of quarter 0 write V.
+  __device__ __forceinline__ void store_new_row(uint16_t* k_dst, uint16_t* v_dst) const {
+    if (r16 == 0) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) f.k[ks] = nk_ov[ks];
-      }
+      for (int ks = 0; ks < NKS; ++ks) *(uint4*)(k_dst + 32 * ks + 8 * q4) = nk_ov[ks];
+    }
+    if (q4 == 0) *(VT*)(v_dst + VW * r16) = nv_ov;
+  }
+
+  // Start the empty online-softmax state from the new row of load_new_row
+  // as its first token, for the rows below G: the reference is the row's
+  // logit (the quarters' partial dot products summed across the four lanes
+  // of a row), its weight exp2(0) = 1 is counted once per row in the
+  // denominator, and O = v_new. Later tokens are added by step() as usual.
+  __device__ __forceinline__ void seed_row(float scale_log2) {
+    using E = Elem<DT>;
+    float d = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (4 * q4 + i == row_new) f.v[i] = nv_ov;
+    for (int ks = 0; ks < NKS; ++ks) {
+      d = E::dot2(qop[ks].x, nk_ov[ks].x, d);
+      d = E::dot2(qop[ks].y, nk_ov[ks].y, d);
+      d = E::dot2(qop[ks].z, nk_ov[ks].z, d);
+      d = E::dot2(qop[ks].w, nk_ov[ks].w, d);
+    }
+    d += __shfl_xor(d, 16);
+    d += __shfl_xor(d, 32);
+    if (r16 < G) {
+      m = d * scale_log2;
+      if (q4 == 0) lsum = 1.0f;
+    }
+    // acc[2k][i], acc[2k+1][i]: head 4*q4+i, columns VW*r16+2k, +2k+1
+    const uint32_t* w = (const uint32_t*)&nv_ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * q4 + i < G) {
+#pragma unroll
+        for (int k = 0; k < VW / 2; ++k) {
+          acc[2 * k][i] = E::lo(w[k]);
+          acc[2 * k + 1][i] = E::hi(w[k]);
+        }
       }
     }
+  }
+
+  // A block with no new-row substitution.
+  __device__ __forceinline__ void process_plain(Frag& f, int tok0, int t_end, float scale_log2) {
+    arrange(f);
     step(f, tok0, r16 < G ? t_end : 0, scale_log2);
   }
 

@@ -71,27 +71,47 @@ struct ValuPolicy {
     compute(f, tok0, t_end, scale_log2);
   }
 
-  // The step's new K/V row loaded straight into registers by the lanes that
-  // read the new token's row (row group row_new % RG); process_own takes it
-  // in place of the pool's row (no LDS, no barrier).
+  // The step's new K/V row (this KV head's D elements) for the planned
+  // kernel: every lane loads chunk c, the chunk its rows cover.
   __device__ __forceinline__ void load_new_row(const uint16_t* nk_row, const uint16_t* nv_row) {
-    if (rg == row_new % RG) {
-      nk_ov = *(const uint4*)(nk_row + 8 * c);
-      nv_ov = *(const uint4*)(nv_row + 8 * c);
+    nk_ov = *(const uint4*)(nk_row + 8 * c);
+    nv_ov = *(const uint4*)(nv_row + 8 * c);
+  }
+
+  // Store the row loaded by load_new_row (the lanes of row group 0).
+  __device__ __forceinline__ void store_new_row(uint16_t* k_dst, uint16_t* v_dst) const {
+    if (rg == 0) {
+      *(uint4*)(k_dst + 8 * c) = nk_ov;
+      *(uint4*)(v_dst + 8 * c) = nv_ov;
     }
   }
 
-  __device__ __forceinline__ void process_own(Frag& f, int tok0, int t_end, float scale_log2,
-                                              bool sub) {
-    if (sub) {
+  // Start the empty online-softmax state from the new row as the first
+  // token, held by row group 0 (each row group keeps its own state until
+  // to_lds merges them): reference = its logit, weight 1, O = v_new.
+  __device__ __forceinline__ void seed_row(float scale_log2) {
+    using E = Elem<DT>;
+    const uint32_t w[4] = {nv_ov.x, nv_ov.y, nv_ov.z, nv_ov.w};
 #pragma unroll
-      for (int i = 0; i < TPL; ++i) {
-        if (i * RG + rg == row_new) {
-          f.k[i] = nk_ov;
-          f.v[i] = nv_ov;
+    for (int j = 0; j < G; ++j) {
+      float d = E::dot2(qv[j].x, nk_ov.x, 0.0f);
+      d = E::dot2(qv[j].y, nk_ov.y, d);
+      d = E::dot2(qv[j].z, nk_ov.z, d);
+      d = E::dot2(qv[j].w, nk_ov.w, d);
+      const float z = group_sum<LPR>(d) * scale_log2;
+      if (rg == 0) {
+        m[j] = z;
+        l[j] = 1.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[j][2 * e] = E::lo(w[e]);
+          acc[j][2 * e + 1] = E::hi(w[e]);
         }
       }
     }
+  }
+
+  __device__ __forceinline__ void process_plain(Frag& f, int tok0, int t_end, float scale_log2) {
     compute(f, tok0, t_end, scale_log2);
   }
 

@@ -31,12 +31,16 @@
 //  * The waves of an item merge their online-softmax states through LDS
 //    (log-sum-exp rule, fixed order) and write the item's rows.
 // Per-block compute is the MFMA tile (g >= 2) or the VALU policy (g = 1).
-// Fused cache write without any barrier: the wave whose blocks include the
-// sequence's new slot loads the step's new K/V row straight into the operand
-// layout and uses it in place of the pool's row, and the item's first wave
-// stores the row into the pools (the store of record). A sequence appends
-// only into its own blocks, which no other sequence reads (the paged
-// allocator's rule), so no other item waits for that store.
+// The fused cache write costs the block loop nothing: in a decode step the
+// new token is the sequence's last position, so the wave holding the last
+// block reads the blocks up to the token before it (the buffer descriptor
+// ends there, so the slot's old bits are never read); that wave starts its
+// online-softmax state from the new row, taken as the first token while its
+// block loads are in flight, and stores the row. A slot elsewhere in the item's blocks
+// is stored first by the wave that reads that block, which waits for the
+// store before its loads; a sequence appends only into its own blocks, which
+// no other sequence reads (the paged allocator's rule), so no other wave
+// depends on the store.
 #include <type_traits>
 
 #include "attention_mfma.h"
@@ -57,7 +61,16 @@ enum : int {
   kDescSlot = 4,      // the sequence's new-token slot (fused cache write), or -1
   kDescWaves = 5,     // first wave of the item (bits 0-7), waves of the item (bits 8-15)
   kDescLen = 6,       // the sequence's context length
+  kDescFlags = 7,     // the wave's part in the fused cache write (kFlag*)
 };
+
+// Parts in the fused cache write (descriptor int kDescFlags), set by the plan
+// per item: when the new slot is the sequence's position L-1 (a decode
+// step's own token), the wave holding the last block stops before it,
+// starts its state from the new row (append), and stores it; when the slot is in one of the item's other blocks, the wave holding
+// that block stores the row first and reads its blocks after the store has
+// completed (store first); otherwise the item's first wave stores it.
+enum : int { kFlagAppend = 1, kFlagStore = 2, kFlagStoreFirst = 4 };
 
 constexpr int kBinThreads = 256;
 
@@ -139,23 +152,22 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
   const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;
   const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
   Policy pol;
-  int slot = -1;
-  if constexpr (FUSED) slot = __builtin_amdgcn_readlane(dv, kDescSlot);
+  int slot = -1, flags = 0;
+  if constexpr (FUSED) {
+    slot = __builtin_amdgcn_readlane(dv, kDescSlot);
+    flags = __builtin_amdgcn_readlane(dv, kDescFlags);
+  }
   const bool has_new = FUSED && in_item && slot >= 0 && slot < sh.num_blocks * kBlockTokens;
-  const int blk_new = has_new ? slot / kBlockTokens : -1;
-  if constexpr (FUSED) pol.row_new = has_new ? slot % kBlockTokens : -1;
-  const bool writer = has_new && wave == wb;  // the store of record: the item's first wave
-  // the wave whose blocks include the new slot's block reads the new row in
-  // place of the pool's
-  const bool holder =
-      has_new && __ballot(lane >= kPlanHdrInts && lane < kPlanHdrInts + nblk && dv == blk_new) != 0;
-  uint4 nk16 = make_uint4(0u, 0u, 0u, 0u), nv16 = nk16;
+  const bool append = has_new && (flags & kFlagAppend);
+  const bool store = has_new && (flags & (kFlagStore | kFlagStoreFirst));
+  const bool store_first = has_new && (flags & kFlagStoreFirst);
+  const size_t new_dst = (size_t)(has_new ? slot : 0) * sh.num_kv_heads * D + (size_t)h * D;
 
   const char* kbase = (const char*)(k_cache + (size_t)h * D);
   const char* vbase = (const char*)(v_cache + (size_t)h * D);
   typename Policy::Frag f[NPF];
   auto block_of = [&](int k) {
-    const int blk = __builtin_amdgcn_readlane(dv, kPlanHdrInts + min(k, nblk - 1));
+    const int blk = __builtin_amdgcn_readlane(dv, kPlanHdrInts + min(k, max(nblk - 1, 0)));
     return ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
   };
   // Rows of block k that hold context tokens are read through its buffer
@@ -164,7 +176,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
   auto load_block = [&](typename Policy::Frag& fr, int k) {
     const bool real = k < nblk;
     const int blk = block_of(k);
-    const int kk = min(k, nblk - 1);
+    const int kk = min(k, max(nblk - 1, 0));
     const int rows = min(kBlockTokens, te - (tb + kk * kBlockTokens));
     const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
     const size_t o = (size_t)blk * block_bytes;
@@ -175,39 +187,55 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
   if (in_item) {
     pol.init(q, (size_t)s * Hq + (size_t)h * G, lane, row_bytes);
     if constexpr (FUSED) {
-      const size_t src = ((size_t)s * sh.num_kv_heads + h) * D;
-      if (writer && lane < D / 8) {
-        nk16 = *(const uint4*)(new_key + src + lane * 8);
-        nv16 = *(const uint4*)(new_value + src + lane * 8);
+      if (append || store) {
+        const size_t src = ((size_t)s * sh.num_kv_heads + h) * D;
+        pol.load_new_row(new_key + src, new_value + src);
       }
-      if (holder) pol.load_new_row(new_key + src, new_value + src);
+      if (store_first) {
+        // the slot lies in one of this wave's blocks: store the row, and let
+        // the block loads below start only once the store has completed
+        pol.store_new_row(k_cache + new_dst, v_cache + new_dst);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
     }
     // Loads complete in issue order: the query and new-row loads go out
     // before the K/V stream, so the first block is computed as soon as it
     // lands instead of after the blocks issued ahead of a late query load.
     __builtin_amdgcn_sched_barrier(0);
-    if (nblk > 0) {
+    // NPF blocks in flight from here on (empty descriptors past the last
+    // block): block k's buffer is refilled with block k + NPF right after
+    // block k is computed.
 #pragma unroll
-      for (int j = 0; j < NPF - 1; ++j) load_block(f[j], j);
-      for (int k0 = 0;; k0 += NPF) {
-#pragma unroll
-        for (int j = 0; j < NPF; ++j) {
-          const int k = k0 + j;
-          load_block(f[(j + NPF - 1) % NPF], k + NPF - 1);
-          pol.process_own(f[j], tb + k * kBlockTokens, te, sh.scale_log2,
-                          holder && block_of(k) == blk_new);
-          if (k + 1 >= nblk) goto blocks_done;
-        }
-      }
-    blocks_done:;
-    }
+    for (int j = 0; j < NPF; ++j) load_block(f[j], j);
     if constexpr (FUSED) {
-      // the store of record (after the blocks: storing earlier would make
-      // this wave wait for the new row before issuing its next K/V loads)
-      if (writer && lane < D / 8) {
-        const size_t dst = (size_t)slot * sh.num_kv_heads * D + (size_t)h * D + lane * 8;
-        *(uint4*)(k_cache + dst) = nk16;
-        *(uint4*)(v_cache + dst) = nv16;
+      // The new token enters the state before any block (it waits only for
+      // the query and new-row loads, while the block loads are in flight),
+      // and its row is stored at once: no wave of this item reads its slot.
+      if (append) pol.seed_row(sh.scale_log2);
+      if (store && !store_first) pol.store_new_row(k_cache + new_dst, v_cache + new_dst);
+    }
+    // Steady state: groups of NPF blocks whose refills are all real blocks,
+    // with no branch around a load, so every path keeps the same loads in
+    // flight and each block waits only for its own. Then the last one or two
+    // groups, which skip the steps and refills past nblk (their waits are
+    // coarser, but a short run gains more from issuing no empty loads).
+    int k = 0;
+    for (; k + 2 * NPF <= nblk; k += NPF) {
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        pol.process_plain(f[j], tb + (k + j) * kBlockTokens, te, sh.scale_log2);
+        // the refill stays behind the block's last reads, so it reuses the
+        // block's registers instead of alternating between two sets
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(f[j], k + j + NPF);
+      }
+    }
+    for (; k < nblk; k += NPF) {
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        if (k + j < nblk) pol.process_plain(f[j], tb + (k + j) * kBlockTokens, te, sh.scale_log2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + j + NPF < nblk) load_block(f[j], k + j + NPF);
       }
     }
   }
@@ -243,22 +271,29 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
   __shared__ int32_t nblk[kPlanMaxSeqs];
   __shared__ int32_t lens[kPlanMaxSeqs];
   __shared__ int32_t slot_of[kPlanMaxSeqs];
+  __shared__ int32_t appends[kPlanMaxSeqs];  // the slot is the sequence's position L-1
   __shared__ __attribute__((aligned(16))) int32_t keys[kPlanMaxSeqs];
   __shared__ int32_t rank_of[kPlanMaxSeqs];
   __shared__ int32_t seq_of_rank[kPlanMaxSeqs];
   __shared__ int32_t hdr[W][kPlanHdrInts];
+  __shared__ int32_t holds[W];  // the wave's blocks include its item's new slot (not at L-1)
   const int t = threadIdx.x;
   const int S = ps.num_seqs;
+  if (t < W) holds[t] = 0;
   const int S4 = (S + 3) & ~3;
   for (int s = t; s < S4; s += kBinThreads) {
     int key = -1;  // padding: never larger than a real key
     if (s < S) {
       const int L = min(max(context_lens[s], 0), ps.max_context_len);
       const int nb = (L + kBlockTokens - 1) / kBlockTokens;
+      const int slot = slots != nullptr ? slots[s] : -1;
       lens[s] = L;
       nblk[s] = nb;
-      slot_of[s] = slots != nullptr ? slots[s] : -1;
+      slot_of[s] = slot;
       rank_of[s] = 0;
+      appends[s] = L > 0 && slot >= 0 &&
+                   slot == block_tables[(size_t)s * ps.max_blocks + (L - 1) / kBlockTokens] *
+                                   kBlockTokens + (L - 1) % kBlockTokens;
       // unique key, larger = earlier: more blocks first, then lower index
       key = (nb << 10) | (kPlanMaxSeqs - 1 - s);
     }
@@ -347,31 +382,50 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
       }
       const int x = t - wb;
       const int b0 = x * nb / wn, b1 = (x + 1) * nb / wn;
+      const bool last = x == wn - 1;
+      const bool app = appends[s] != 0;
       hw[kDescSeq] = s;
       hw[kDescHead] = h;
       hw[kDescTokBegin] = b0 * kBlockTokens;
-      hw[kDescTokEnd] = min(b1 * kBlockTokens, lens[s]);
+      // the append wave's blocks end before the new token
+      hw[kDescTokEnd] = min(b1 * kBlockTokens, lens[s] - (app && last ? 1 : 0));
       hw[kDescSlot] = slot_of[s];
       hw[kDescWaves] = wb | (wn << 8);
       hw[kDescLen] = lens[s];
-      hw[7] = 0;
+      // provisional: the store-first holder, if any, is found below
+      hw[kDescFlags] = slot_of[s] < 0 ? 0
+                       : app ? (last ? kFlagAppend | kFlagStore : 0)
+                             : (x == 0 ? kFlagStore : 0);
     }
   }
   __syncthreads();
+  // block ids; a wave whose blocks include its item's new slot (when that is
+  // not the append case) is marked as the store-first holder
+  int32_t* desc = plan + (size_t)blockIdx.x * W * kPlanDescInts;
   for (int idx = t; idx < W * kPlanDescInts; idx += kBinThreads) {
     const int w = idx / kPlanDescInts;
     const int k = idx % kPlanDescInts;
-    int v;
-    if (k < kPlanHdrInts) {
-      v = hdr[w][k];
-    } else {
-      const int s = hdr[w][kDescSeq];
-      const int tb = hdr[w][kDescTokBegin];
-      const int n = s >= 0 ? max(hdr[w][kDescTokEnd] - tb + kBlockTokens - 1, 0) / kBlockTokens : 0;
-      const int j = k - kPlanHdrInts;
-      v = j < n ? block_tables[(size_t)s * ps.max_blocks + tb / kBlockTokens + j] : -1;
+    if (k < kPlanHdrInts) continue;
+    const int s = hdr[w][kDescSeq];
+    const int tb = hdr[w][kDescTokBegin];
+    const int n = s >= 0 ? max(hdr[w][kDescTokEnd] - tb + kBlockTokens - 1, 0) / kBlockTokens : 0;
+    const int j = k - kPlanHdrInts;
+    const int v = j < n ? block_tables[(size_t)s * ps.max_blocks + tb / kBlockTokens + j] : -1;
+    if (j < n && slot_of[s] >= 0 && !appends[s] && v == slot_of[s] / kBlockTokens) holds[w] = 1;
+    desc[idx] = v;
+  }
+  __syncthreads();
+  if (t < W) {
+    int flags = hdr[t][kDescFlags];
+    const int s = hdr[t][kDescSeq];
+    if (s >= 0 && slot_of[s] >= 0 && !appends[s]) {
+      const int wb = hdr[t][kDescWaves] & 0xff, wn = (hdr[t][kDescWaves] >> 8) & 0xff;
+      bool any = false;
+      for (int w = wb; w < wb + wn; ++w) any = any || holds[w] != 0;
+      if (any) flags = holds[t] ? kFlagStoreFirst : 0;   // the holder stores, nobody else
     }
-    plan[((size_t)blockIdx.x * W + w) * kPlanDescInts + k] = v;
+#pragma unroll
+    for (int k = 0; k < kPlanHdrInts; ++k) desc[t * kPlanDescInts + k] = k == kDescFlags ? flags : hdr[t][k];
   }
 }
 

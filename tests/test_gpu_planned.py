@@ -101,6 +101,84 @@ def test_planned_items_longer_than_one_descriptor(dtype, D, hq, hkv):
     check_layer(wl, 0, False, f"long items {dtype} D={D} g={hq // hkv}")
 
 
+def planned_fused(wl, slots):
+    """Planned call with the fused write at `slots` on fresh GPU copies:
+    (out, k pool bits, v pool bits)."""
+    g = wl.to("cuda")
+    l = g.layers[0]
+    sm = slots.cuda()
+    maxlen = wl.max_context_len
+    plan = mvk.make_plan(g.block_tables, g.context_lens, wl.num_q_heads, wl.num_kv_heads,
+                         wl.head_dim, maxlen, slot_mapping=sm)
+    out = mvk.paged_attention_decode_planned(l.q, l.k_cache, l.v_cache, plan, wl.scale, maxlen,
+                                             new_key=l.key, new_value=l.value)
+    torch.cuda.synchronize()
+    return out, bits(l.k_cache), bits(l.v_cache)
+
+
+def check_planned_fused(wl, slots, label):
+    """Against the oracle's write-then-decode: pools bit-exact, output within
+    the bar, bits repeatable."""
+    layer = wl.layers[0]
+    ek, ev = oracle.cache_write(bits(layer.k_cache), bits(layer.v_cache), bits(layer.key),
+                                bits(layer.value), slots.numpy())
+    ref = oracle_decode_all(bits(layer.q), ek, ev, wl.block_tables.numpy(),
+                            wl.context_lens.numpy(), wl.scale, wl.dtype)
+    out, k, v = planned_fused(wl, slots)
+    assert np.array_equal(k, ek) and np.array_equal(v, ev), "fused store is not bit-exact"
+    err = max_err(out, ref, wl.dtype)
+    print(f"planned fused {label}: max abs err {err:.3e}", flush=True)
+    assert err <= TOL[wl.dtype], label
+    out2, _, _ = planned_fused(wl, slots)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def poison_slots(wl, slots):
+    """NaN in the rows the cache write is about to replace: the call must
+    not read their old bits."""
+    nan = W.NAN_BITS[wl.dtype]
+    for pool in (wl.layers[0].k_cache, wl.layers[0].v_cache):
+        raw = pool.view(torch.int16).view(-1, wl.num_kv_heads * wl.head_dim)
+        for sl in slots.tolist():
+            if sl >= 0:
+                raw[sl] = nan
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+def test_planned_fused_newest_token(dtype, d, g):
+    """The decode step's own token (the slot of position L-1): appended after
+    the blocks, including contexts where it is alone in its block (L = 17,
+    33) and the one-token context (the output is the new V row)."""
+    lens = [1, 16, 17, 100, 255, 33, 2, 640]
+    nb = sum(-(-L // 16) for L in lens) + 5
+    wl = W.make_custom("pf", dtype, lens, 2 * g, 2, d, nb, seed=70 + g)
+    W.poison_unread(wl)
+    poison_slots(wl, wl.slot_mapping)
+    check_planned_fused(wl, wl.slot_mapping, f"newest {dtype} D={d} g={g}")
+
+
+@pytest.mark.parametrize("g", [1, 2, 4])
+def test_planned_fused_other_slots(g):
+    """Slots at an early position of the sequence's own context and at the
+    first row of its last block (stored first by the wave that reads that
+    block), in a block nobody reads, and negative (no write)."""
+    lens = [40, 70, 5, 130, 16, 900]
+    nb = sum(-(-L // 16) for L in lens) + 3
+    wl = W.make_custom("pf", "bf16", lens, 2 * g, 2, 128, nb, seed=80 + g)
+    bt = wl.block_tables
+    used = set(int(x) for x in wl.used_block_ids())
+    free_blk = next(b for b in range(nb) if b not in used)
+    slots = wl.slot_mapping.clone()
+    slots[0] = int(bt[0, 0]) * 16 + 3            # an early token of its own context
+    slots[1] = int(bt[1, 4]) * 16 + 0            # first row of its last block
+    slots[2] = free_blk * 16 + 7                 # a block nobody reads
+    slots[3] = -1                                # no write this step
+    slots[5] = int(bt[5, 20]) * 16 + 9           # a middle block of a many-wave item
+    poison_slots(wl, slots)
+    check_planned_fused(wl, slots, f"other slots g={g}")
+
+
 def test_planned_is_deterministic_and_poison_proof():
     lens = [5, 300, 17, 129, 64, 1, 250, 33]
     wl = W.make_custom("p", "f16", lens, 16, 4, 64, 60, 400)
