@@ -340,7 +340,8 @@ def time_config(torch, mvk, W, dev, name, reps):
     """Per-call time of another workload's decode call (cache write fused,
     planned where the library covers the batch), back to back in a graph over
     its rotating pool sets; bytes and roofline fraction as for the main
-    line."""
+    line; the plan's own time per step (one plan serves every layer of a
+    step) beside it."""
     wl = W.make(name, value_device="cuda")
     layers = list(wl.layers)
     for extra in range(1, POOL_SETS.get(name, 1)):
@@ -351,12 +352,15 @@ def time_config(torch, mvk, W, dev, name, reps):
     torch.cuda.synchronize()
     us = graph_time_per_call(torch, dev, [lambda li=li: dec.call(li)
                                           for li in range(len(layers))], reps)
+    plan_us = (graph_time_per_call(torch, dev, [dec.make_plan] * 8, reps)
+               if dec.planned else None)
     acc = decode_bytes(torch, wl, dec.fused)
     gbs = acc["call_alg"] / (us * 1e-6) / 1e9
     out = {"workload": WORKLOAD_TEXT[name], "planned": dec.planned,
            "partition_tokens": dec.partition, "launch_us": round(us, 3),
            "alg_bytes_per_launch": acc["call_alg"], "achieved_gbs": round(gbs, 1),
            "frac": round(gbs / HBM_PEAK_GBS, 4), "pool_sets": POOL_SETS.get(name, 1),
+           "plan_us_per_step": None if plan_us is None else round(plan_us, 3),
            "traffic": measured_traffic(name, True, kind="paged_decode_planned" if dec.planned
                                        else "paged_decode")}
     del dec, layers, wl
@@ -622,7 +626,6 @@ def kernel_source_digest(kind="paged_decode"):
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_206_amd",
                         "csrc")
     base = kind.split("_n")[0] if kind.startswith("paged_multi_query") else kind
-    base = base[:-len("_unfused")] if base.endswith("_unfused") else base
     todo, seen = [KERNEL_SOURCES[base], "api.hip"], set()
     while todo:
         name = todo.pop()

@@ -225,8 +225,8 @@ int32_t mvk_paged_attention_decode(void* out, const void* q,
  * ranking or table walk.
  *
  * Scope: single-pass batches (each (sequence, KV head) item is done by one
- * workgroup): at most 1024 sequences, and contexts short enough for the
- * items of a workgroup (mvk_paged_attention_plan_size returns
+ * workgroup): at most 1024 sequences and 256 KV heads, and contexts short
+ * enough for the items of a workgroup (mvk_paged_attention_plan_size returns
  * MVK_ERR_UNSUPPORTED otherwise; mvk_paged_attention_decode covers every
  * batch). The plan is a snapshot: it holds copies of the block ids, lengths
  * and slots as they are when the plan kernel runs (stream order); later

@@ -235,6 +235,7 @@ constexpr int32_t kCus = 256;
 
 struct PlanGeom {
   int32_t bins;
+  int32_t desc_ints;
   size_t bytes;
 };
 
@@ -246,7 +247,7 @@ int32_t plan_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
   if (num_q_heads % num_kv_heads != 0) return MVK_ERR_INVALID_ARGUMENT;
   const int32_t group = num_q_heads / num_kv_heads;
   if (!mvk::decode_supported(head_dim, group)) return MVK_ERR_UNSUPPORTED;
-  if (num_seqs > mvk::kPlanMaxSeqs) return MVK_ERR_UNSUPPORTED;
+  if (num_seqs > mvk::kPlanMaxSeqs || num_kv_heads > mvk::kPlanMaxKvHeads) return MVK_ERR_UNSUPPORTED;
   const int64_t items = (int64_t)num_seqs * num_kv_heads;
   const int32_t waves_per_simd = (head_dim == 64 || group == 1) ? 4 : 2;
   const int64_t cap = (int64_t)kCus * (4 * waves_per_simd / mvk::kPlanWaves);
@@ -263,7 +264,9 @@ int32_t plan_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
   if (bins > items) bins = items;
   if (bins > INT32_MAX / (mvk::kPlanWaves * mvk::kPlanDescInts)) return MVK_ERR_UNSUPPORTED;
   g->bins = (int32_t)bins;
-  g->bytes = (size_t)bins * mvk::kPlanWaves * mvk::kPlanDescInts * 4u;
+  g->desc_ints = blocks <= mvk::kPlanShortDescInts - mvk::kPlanHdrInts ? mvk::kPlanShortDescInts
+                                                                      : mvk::kPlanDescInts;
+  g->bytes = (size_t)bins * mvk::kPlanWaves * g->desc_ints * 4u;
   return MVK_OK;
 }
 
@@ -521,6 +524,7 @@ int32_t mvk_paged_attention_plan(void* plan, size_t plan_bytes, const int32_t* b
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
   a.num_bins = g.bins;
+  a.desc_ints = g.desc_ints;
   const hipError_t err = mvk::launch_decode_plan(a, (hipStream_t)stream);
   return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
 }
@@ -568,6 +572,7 @@ int32_t mvk_paged_attention_decode_planned(void* out, const void* q, void* k_cac
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.num_bins = g.bins;
+  a.desc_ints = g.desc_ints;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.dtype = dtype;
   const hipError_t err = mvk::launch_paged_decode_planned(a, (hipStream_t)stream);

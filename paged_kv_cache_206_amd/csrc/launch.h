@@ -61,12 +61,17 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Planned single-pass decode: a plan built once per decode step (block
 // tables, lengths and new-token slots of the step) that every layer's call
-// reads. The plan is num_bins * kPlanWaves descriptors of kPlanDescInts ints.
-constexpr int32_t kPlanWaves = 8;        // waves per bin (workgroup)
-constexpr int32_t kPlanDescInts = 64;    // ints per wave descriptor
-constexpr int32_t kPlanHdrInts = 8;      // descriptor header; the rest are block ids
+// reads. The plan is num_bins * kPlanWaves descriptors of desc_ints ints:
+// kPlanShortDescInts (one 128-byte line) when no sequence has more than
+// kPlanShortDescInts - kPlanHdrInts blocks, kPlanDescInts otherwise, so a
+// batch of short contexts reads half the plan bytes per call.
+constexpr int32_t kPlanWaves = 8;          // waves per bin (workgroup)
+constexpr int32_t kPlanDescInts = 64;      // ints per wave descriptor (longest form)
+constexpr int32_t kPlanShortDescInts = 32;  // the short form
+constexpr int32_t kPlanHdrInts = 8;        // descriptor header; the rest are block ids
 constexpr int32_t kPlanMaxBlocks = kPlanDescInts - kPlanHdrInts;  // blocks per wave
 constexpr int32_t kPlanMaxSeqs = 1024;   // sequences one plan ranks (in LDS)
+constexpr int32_t kPlanMaxKvHeads = 256;  // KV heads of a planned batch
 
 struct DecodePlanArgs {
   int32_t* plan;
@@ -74,6 +79,7 @@ struct DecodePlanArgs {
   const int32_t* context_lens;
   const int32_t* slot_mapping;  // nullptr: no new-token slots recorded
   int32_t num_seqs, num_kv_heads, max_blocks_per_seq, max_context_len, num_bins;
+  int32_t desc_ints;  // kPlanShortDescInts or kPlanDescInts
 };
 
 hipError_t launch_decode_plan(const DecodePlanArgs& a, hipStream_t stream);
@@ -87,6 +93,7 @@ struct PlannedDecodeArgs {
   const void* new_value;
   const int32_t* plan;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_context_len, num_bins;
+  int32_t desc_ints;  // the plan's descriptor size
   float scale_log2;
   int32_t dtype;
 };

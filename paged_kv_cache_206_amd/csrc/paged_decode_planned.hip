@@ -23,11 +23,13 @@
 //    each item gets the waves its descriptors need, then every spare wave
 //    goes to the item whose waves carry the most blocks each), and each wave
 //    takes a contiguous run of its item's blocks.
-//  * Each wave's work is one 64-int descriptor: sequence, KV head, token
-//    range, the sequence's new-token slot and context length, its item's
-//    wave range, and the physical ids of its blocks (copied from the block
-//    table). The decode kernel's wave fetches it with one load, so K/V loads
-//    start after a single round trip, and no wave ranks or searches anything.
+//  * Each wave's work is one descriptor: sequence, KV head, token range,
+//    the sequence's new-token slot and context length, its item's wave
+//    range, and the physical ids of its blocks (copied from the block
+//    table); 32 ints (one 128-byte line, up to 24 blocks) when no sequence
+//    has more blocks, 64 otherwise. The decode kernel's wave fetches it with
+//    one load, so K/V loads start after a single round trip, and no wave
+//    ranks or searches anything.
 //  * The waves of an item merge their online-softmax states through LDS
 //    (log-sum-exp rule, fixed order) and write the item's rows.
 // Per-block compute is the MFMA tile (g >= 2) or the VALU policy (g = 1).
@@ -52,7 +54,7 @@ namespace mvk {
 
 namespace {
 
-// Descriptor fields (ints 0..7); ints 8..63 are block ids.
+// Descriptor fields (ints 0..7); the rest (24 or 56 ints) are block ids.
 enum : int {
   kDescSeq = 0,       // sequence (negative: idle wave)
   kDescHead = 1,      // KV head
@@ -79,6 +81,7 @@ constexpr int kPlannedWavesPerSimd = (D == 64 || G == 1) ? 4 : 2;
 
 struct PlannedShape {
   int32_t num_seqs, num_kv_heads, num_blocks, max_context_len;
+  int32_t desc_ints;  // kPlanShortDescInts or kPlanDescInts
   float scale_log2;
 };
 
@@ -130,8 +133,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  // lane k holds descriptor int k
-  const int dv = plan[((size_t)blockIdx.x * W + wave) * kPlanDescInts + lane];
+  // lane k holds descriptor int k (lanes past a short descriptor load nothing)
+  const int dv = lane < sh.desc_ints ? plan[((size_t)blockIdx.x * W + wave) * sh.desc_ints + lane] : -1;
   const int s_raw = __builtin_amdgcn_readlane(dv, kDescSeq);
   const int h_raw = __builtin_amdgcn_readlane(dv, kDescHead);
   // every field is clamped into range, so an inconsistent plan gives wrong
@@ -142,7 +145,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
   const int L = min(max(__builtin_amdgcn_readlane(dv, kDescLen), 0), sh.max_context_len);
   const int tb = min(max(__builtin_amdgcn_readlane(dv, kDescTokBegin), 0), L) & ~(kBlockTokens - 1);
   const int te = min(max(__builtin_amdgcn_readlane(dv, kDescTokEnd), tb), L);
-  const int nblk = active ? min((te - tb + kBlockTokens - 1) / kBlockTokens, kPlanMaxBlocks) : 0;
+  const int nblk =
+      active ? min((te - tb + kBlockTokens - 1) / kBlockTokens, sh.desc_ints - kPlanHdrInts) : 0;
   const int wv = __builtin_amdgcn_readlane(dv, kDescWaves);
   const int wb = min(wv & 0xff, W - 1);
   const int wn = min(max((wv >> 8) & 0xff, 1), W - wb);
@@ -262,7 +266,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
 // descriptors; workgroups do not communicate.
 struct BinShape {
   int32_t num_seqs, num_kv_heads, max_blocks, max_context_len, num_bins;
+  int32_t desc_ints;  // kPlanShortDescInts or kPlanDescInts
 };
+static_assert((uint64_t)kPlanMaxSeqs * kPlanMaxKvHeads * kPlanMaxKvHeads < (1ull << 32),
+              "the plan's multiply-high division needs i * num_kv_heads < 2^32");
 
 template <int W>
 __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
@@ -281,7 +288,18 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
   const int S = ps.num_seqs;
   if (t < W) holds[t] = 0;
   const int S4 = (S + 3) & ~3;
-  for (int s = t; s < S4; s += kBinThreads) {
+  // Each thread's sequences (at most kPlanMaxSeqs / kBinThreads): the block
+  // that holds position L-1 is loaded here and compared only after the
+  // ranking, so that load's round trip overlaps the LDS work (the barriers
+  // below order LDS only and leave global loads in flight).
+  constexpr int kPer = kPlanMaxSeqs / kBinThreads;
+  int tail_blk[kPer], tail_slot[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int s = t + r * kBinThreads;
+    tail_blk[r] = -1;
+    tail_slot[r] = -1;
+    if (s >= S4) continue;
     int key = -1;  // padding: never larger than a real key
     if (s < S) {
       const int L = min(max(context_lens[s], 0), ps.max_context_len);
@@ -291,15 +309,16 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
       nblk[s] = nb;
       slot_of[s] = slot;
       rank_of[s] = 0;
-      appends[s] = L > 0 && slot >= 0 &&
-                   slot == block_tables[(size_t)s * ps.max_blocks + (L - 1) / kBlockTokens] *
-                                   kBlockTokens + (L - 1) % kBlockTokens;
+      if (L > 0 && slot >= 0) {
+        tail_blk[r] = block_tables[(size_t)s * ps.max_blocks + (L - 1) / kBlockTokens];
+        tail_slot[r] = (L - 1) % kBlockTokens;
+      }
       // unique key, larger = earlier: more blocks first, then lower index
       key = (nb << 10) | (kPlanMaxSeqs - 1 - s);
     }
     keys[s] = key;
   }
-  __syncthreads();
+  lds_barrier();
   // rank = number of larger keys (a permutation of 0..S-1). Sequence s gets
   // P = 256 / S threads (at least one), each counting over its slice of the
   // keys four at a time; the slices' counts meet in LDS.
@@ -312,6 +331,7 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
       const int mine = keys[s];
       const int c1 = min(chunks, (p + 1) * per);
       int cnt = 0;
+#pragma unroll 8
       for (int c = p * per; c < c1; ++c) {
         const int4 k4 = *(const int4*)(keys + 4 * c);
         cnt += (k4.x > mine) + (k4.y > mine) + (k4.z > mine) + (k4.w > mine);
@@ -319,9 +339,17 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
       if (cnt) atomicAdd(&rank_of[s], cnt);
     }
   }
-  __syncthreads();
-  for (int s = t; s < S; s += kBinThreads) seq_of_rank[rank_of[s]] = s;
-  __syncthreads();
+  lds_barrier();
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int s = t + r * kBinThreads;
+    if (s < S) {
+      seq_of_rank[rank_of[s]] = s;
+      // the slot is the sequence's position L-1
+      appends[s] = tail_blk[r] >= 0 && slot_of[s] == tail_blk[r] * kBlockTokens + tail_slot[r];
+    }
+  }
+  lds_barrier();
   if (t < W) {
     // Every one of the first W threads assembles the bin (the same answer,
     // in registers, with loops over the W possible item slots) and writes
@@ -329,19 +357,27 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
     // round reaches this bin.
     const int N = S * ps.num_kv_heads;
     const int B = ps.num_bins;
+    const int max_ids = ps.desc_ints - kPlanHdrInts;  // block ids a descriptor holds
     const int b = blockIdx.x;
+    // i / num_kv_heads as a multiply-high by the reciprocal rounded up,
+    // ceil(2^32 / hkv): exact while i * hkv < 2^32, which holds for
+    // i < kPlanMaxSeqs * kPlanMaxKvHeads (one head needs no division: its
+    // reciprocal does not fit in 32 bits)
+    const uint32_t hkv = (uint32_t)ps.num_kv_heads;
+    const uint32_t rcp = hkv > 1u ? 0xFFFFFFFFu / hkv + 1u : 0u;
     int is[W], ih[W], inb[W], iw[W];
     int used = 0;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
       const int i = k * B + ((k & 1) ? B - 1 - b : b);
       const bool ok = k * B < N && i < N;
-      const int s = ok ? seq_of_rank[i / ps.num_kv_heads] : 0;
+      const int r = hkv > 1u ? (int)__umulhi((uint32_t)i, rcp) : i;
+      const int s = ok ? seq_of_rank[r] : 0;
       is[k] = s;
-      ih[k] = ok ? i % ps.num_kv_heads : 0;
+      ih[k] = ok ? i - r * (int)hkv : 0;
       inb[k] = ok ? nblk[s] : 0;
       // every item gets the waves its descriptors need (at least one)
-      iw[k] = ok ? max(1, (inb[k] + kPlanMaxBlocks - 1) / kPlanMaxBlocks) : 0;
+      iw[k] = ok ? max(1, (inb[k] + max_ids - 1) / max_ids) : 0;
       used += iw[k];
     }
     // each spare wave goes to the item whose waves carry the most blocks
@@ -398,13 +434,14 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
                              : (x == 0 ? kFlagStore : 0);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // block ids; a wave whose blocks include its item's new slot (when that is
   // not the append case) is marked as the store-first holder
-  int32_t* desc = plan + (size_t)blockIdx.x * W * kPlanDescInts;
-  for (int idx = t; idx < W * kPlanDescInts; idx += kBinThreads) {
-    const int w = idx / kPlanDescInts;
-    const int k = idx % kPlanDescInts;
+  const int dn = ps.desc_ints;
+  int32_t* desc = plan + (size_t)blockIdx.x * W * dn;
+  for (int idx = t; idx < W * dn; idx += kBinThreads) {
+    const int w = idx / dn;
+    const int k = idx % dn;
     if (k < kPlanHdrInts) continue;
     const int s = hdr[w][kDescSeq];
     const int tb = hdr[w][kDescTokBegin];
@@ -414,7 +451,7 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
     if (j < n && slot_of[s] >= 0 && !appends[s] && v == slot_of[s] / kBlockTokens) holds[w] = 1;
     desc[idx] = v;
   }
-  __syncthreads();
+  lds_barrier();
   if (t < W) {
     int flags = hdr[t][kDescFlags];
     const int s = hdr[t][kDescSeq];
@@ -425,13 +462,14 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
       if (any) flags = holds[t] ? kFlagStoreFirst : 0;   // the holder stores, nobody else
     }
 #pragma unroll
-    for (int k = 0; k < kPlanHdrInts; ++k) desc[t * kPlanDescInts + k] = k == kDescFlags ? flags : hdr[t][k];
+    for (int k = 0; k < kPlanHdrInts; ++k) desc[t * dn + k] = k == kDescFlags ? flags : hdr[t][k];
   }
 }
 
 template <int DT, int D, int G, int W, int NPF, bool MFMA>
 hipError_t launch_planned_typed(const PlannedDecodeArgs& a, hipStream_t stream) {
-  PlannedShape sh{a.num_seqs, a.num_kv_heads, a.num_blocks, a.max_context_len, a.scale_log2};
+  PlannedShape sh{a.num_seqs, a.num_kv_heads, a.num_blocks, a.max_context_len, a.desc_ints,
+                  a.scale_log2};
   if (a.new_key != nullptr) {
     hipLaunchKernelGGL((paged_decode_planned_kernel<DT, D, G, W, NPF, MFMA, true>),
                        dim3((unsigned)a.num_bins), dim3(W * 64), 0, stream, (uint16_t*)a.out,
@@ -473,7 +511,8 @@ hipError_t launch_planned_dim(const PlannedDecodeArgs& a, int group, hipStream_t
 }  // namespace
 
 hipError_t launch_decode_plan(const DecodePlanArgs& a, hipStream_t stream) {
-  BinShape ps{a.num_seqs, a.num_kv_heads, a.max_blocks_per_seq, a.max_context_len, a.num_bins};
+  BinShape ps{a.num_seqs, a.num_kv_heads, a.max_blocks_per_seq, a.max_context_len, a.num_bins,
+              a.desc_ints};
   hipLaunchKernelGGL((paged_decode_plan_bins_kernel<kPlanWaves>), dim3((unsigned)a.num_bins),
                      dim3(kBinThreads), 0, stream, a.plan, a.block_tables, a.context_lens,
                      a.slot_mapping, ps);

@@ -210,20 +210,26 @@ def test_plan_scope_and_size(mvk):
     """The planned path covers single-pass batches: one bin per CU (256) of 8
     waves at head_dim 128 with g >= 2, two per CU elsewhere, more when the
     items would not fit their waves, never more bins than (sequence, KV head)
-    items; 64 ints per wave. Contexts over 7168 tokens and more than 1024
-    sequences are outside it."""
-    assert mvk.plan_size(60, 16, 8, 128, 256) == 256 * 8 * 64 * 4        # Qwen3 shape
+    items; 32 ints per wave when no sequence has more than 24 blocks, 64
+    otherwise. Contexts over 7168 tokens, more than 1024
+    sequences and more than 256 KV heads are outside it."""
+    assert mvk.plan_size(60, 16, 8, 128, 256) == 256 * 8 * 32 * 4        # Qwen3 shape
     assert mvk.plan_size(256, 32, 4, 64, 2048) == 512 * 8 * 64 * 4       # TinyLlama shape
-    assert mvk.plan_size(4, 4, 2, 64, 45) == 8 * 8 * 64 * 4              # tiny: one bin per item
+    assert mvk.plan_size(4, 4, 2, 64, 45) == 8 * 8 * 32 * 4              # tiny: one bin per item
     assert mvk.plan_size(0, 4, 2, 64, 45) == 0
     assert mvk.plan_size(32, 32, 8, 128, 32768) is None                  # Llama-7B long
     assert mvk.plan_size(512, 16, 8, 128, 131072) is None                # skewed
     assert mvk.plan_size(1025, 4, 2, 64, 45) is None
+    assert mvk.plan_size(4, 256, 256, 64, 45) == 512 * 8 * 32 * 4       # 256 KV heads: 1024 items
+    assert mvk.plan_size(4, 257, 257, 64, 45) is None
     # more items than the resident bins hold: 8 items per bin, 257 bins
-    assert mvk.plan_size(257, 16, 8, 128, 300) == 257 * 8 * 64 * 4
+    assert mvk.plan_size(257, 16, 8, 128, 300) == 257 * 8 * 32 * 4
     # items needing three waves (up to 168 blocks): two items per bin
     assert mvk.plan_size(300, 8, 8, 128, 2600) == 1200 * 8 * 64 * 4
     assert mvk.plan_size(4, 4, 2, 64, 7168) == 8 * 8 * 64 * 4
+    # the short descriptor holds 24 blocks: 384 tokens, one more takes the long form
+    assert mvk.plan_size(4, 4, 2, 64, 384) == 8 * 8 * 32 * 4
+    assert mvk.plan_size(4, 4, 2, 64, 385) == 8 * 8 * 64 * 4
     assert mvk.plan_size(4, 4, 2, 64, 7169) is None
     with pytest.raises(mvk.MvkError):
         mvk.plan_size(4, 6, 4, 64, 45)

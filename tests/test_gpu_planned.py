@@ -69,6 +69,7 @@ MIXED = [0, 1, 15, 16, 17, 31, 32, 33, 100, 255, 256, 257, 640, 1, 0, 48]
     ("bf16", 128, 16, 8), ("f16", 64, 8, 4),          # g = 2
     ("f16", 128, 16, 4), ("bf16", 64, 32, 8),         # g = 4
     ("f16", 64, 32, 4), ("bf16", 128, 64, 8),         # g = 8
+    ("bf16", 128, 8, 1), ("f16", 64, 6, 3),           # one KV head; three (item -> sequence division)
 ])
 def test_planned_sweep(dtype, D, hq, hkv, fused):
     lens = [L if L > 0 else (0 if not fused else 1) for L in MIXED]
@@ -89,6 +90,17 @@ def test_planned_writes_every_row_once(num_seqs):
     wl = W.make_custom("p", "bf16", lens.tolist(), 16, 8, 128,
                        int(((lens + 15) // 16).sum()) + 3, 300 + num_seqs, new_rows=False)
     check_layer(wl, 0, False, f"{num_seqs} seqs")
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused_write"])
+def test_planned_short_descriptors_at_capacity(fused):
+    """Short (32-int) descriptors at their limit: 258 sequences fill every
+    bin with eight one-wave items, and contexts of 384, 383 and 369 tokens
+    put 24 blocks (the short form's capacity) in one descriptor."""
+    lens = [384, 383, 369, 1, 17, 200] * 43
+    wl = W.make_custom("p", "bf16", lens, 16, 8, 128, sum(-(-L // 16) for L in lens) + 3, 77)
+    assert mvk.plan_size(wl.num_seqs, 16, 8, 128, wl.max_context_len) == 258 * 8 * 32 * 4
+    check_layer(wl, 0, fused, "short descriptors at capacity")
 
 
 @pytest.mark.parametrize("dtype,D,hq,hkv", [("bf16", 128, 8, 8), ("f16", 64, 32, 4)])
