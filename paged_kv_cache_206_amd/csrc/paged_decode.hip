@@ -248,11 +248,26 @@ __device__ __forceinline__ void decode_item(
   // result does not depend on arrival order, and resets the counter to zero
   // for the next call. No workgroup ever waits for another.
   //
-  // The partial states are written and read only with device-coherent
-  // accesses (publish / collect), so no cache-wide fence is needed: a device
-  // release or acquire fence would write back or invalidate this XCD's whole
-  // L2, which costs more than the merge saves. Waiting for every store of the
-  // workgroup to complete before the counter update orders them before it.
+  // Memory ordering. The partial states are written and read only with
+  // agent-scope atomic stores and loads (publish / collect: sc1 accesses,
+  // coherent across the XCDs' L2s by themselves), so the two halves of a
+  // release / acquire pair that the merge needs are done explicitly instead
+  // of with agent-scope fences, which would write back or invalidate this
+  // XCD's whole L2 and cost more than the merge saves:
+  //  * writer: every wave waits for its own publish stores to complete
+  //    (s_waitcnt vmcnt(0): a store counts as complete once it is visible at
+  //    agent scope), then the barrier, then one thread's counter increment
+  //    (an agent-scope atomic read-modify-write). The barrier also keeps the
+  //    compiler from moving the increment above the waits. So every store a
+  //    workgroup published is visible device-wide before its increment is.
+  //  * reader: the workgroup whose increment returns parts - 1 has seen every
+  //    other increment of this counter before its own, hence every store
+  //    published before them. Its collect loads are issued only after the
+  //    increment returned (its value reaches them through LDS, a barrier and
+  //    a branch; the GPU does not issue loads speculatively), and as
+  //    agent-scope loads they cannot be served from a stale cache line.
+  // The counter is reset by that workgroup; the next call is a later kernel,
+  // ordered after this one by the stream.
   if (parts_of_seq > 1 && counters != nullptr) {
     int32_t* ctr = counters + (size_t)s * sh.num_kv_heads + h;
     __builtin_amdgcn_s_waitcnt(0);
