@@ -9,8 +9,8 @@
 // over the prompt's tokens 0..t, and every token's K/V row goes to the slot
 // the block manager gave it (same page, "2. 分页KV缓存（PagedAttention）").
 //
-// Work decomposition: one workgroup of W = 4 waves per (32 W query tokens,
-// query head, prompt). Wave w owns two 16-row tiles, query tokens [16w, 16w +
+// Work decomposition: one workgroup of W waves (4, or 8 at head_dim 128) per
+// (32 W query tokens, query head, prompt). Wave w owns two 16-row tiles, query tokens [16w, 16w +
 // 16) and [16W + 16w, 16W + 16w + 16) of the workgroup's range, so the waves reach
 // the causal diagonal at similar depths. The workgroup walks the prompt's K/V
 // rows from token 0 to its last query token in 64-token tiles, double
@@ -90,7 +90,11 @@ __device__ __forceinline__ int vt_pos(int t) {
 
 template <int DT, int D>
 struct PfTile {
-  static constexpr int kWaves = 4;                 // waves per workgroup
+  // waves per workgroup: eight at D = 128, where registers allow two per
+  // SIMD either way: one workgroup then stages each K/V tile for 256 query
+  // rows instead of two workgroups staging it for 128 each (half the L2
+  // traffic and staging work)
+  static constexpr int kWaves = D == 128 ? 8 : 4;
   static constexpr int kTiles = 2;                 // 16-row query tiles per wave
   static constexpr int kRows = 16 * kTiles * kWaves;  // query tokens per workgroup
   static constexpr int kKvTile = 64;               // K/V tokens per LDS tile
