@@ -410,7 +410,11 @@ def read_ceiling(torch, mvk, dev, call_bytes, ncalls, reps):
 
 def graph_time_per_call(torch, dev, calls, reps):
     """Mean time per call of `calls` (a list of thunks) captured back to back in
-    one HIP graph, with one event pair on the stream around all replays."""
+    one HIP graph, with one event pair on the stream around all replays. The
+    list is repeated until the graph holds at least 8 calls, as a step's graph
+    does, so that the gap between one replay and the next is spread over
+    several calls rather than charged to a single one."""
+    calls = list(calls) * max(1, -(-8 // len(calls)))
     cur = torch.cuda.current_stream(dev)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):

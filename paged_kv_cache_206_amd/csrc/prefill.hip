@@ -9,7 +9,8 @@
 // over the prompt's tokens 0..t, and every token's K/V row goes to the slot
 // the block manager gave it (same page, "2. 分页KV缓存（PagedAttention）").
 //
-// Work decomposition: one workgroup of W waves (4, or 8 at head_dim 128) per
+// Work decomposition: one workgroup of W waves (4, or 8 at head_dim 128 for
+// prompts of 2048 tokens or more) per
 // (32 W query tokens, query head, prompt). Wave w owns two 16-row tiles, query tokens [16w, 16w +
 // 16) and [16W + 16w, 16W + 16w + 16) of the workgroup's range, so the waves reach
 // the causal diagonal at similar depths. The workgroup walks the prompt's K/V
@@ -88,13 +89,15 @@ __device__ __forceinline__ int vt_pos(int t) {
   return 32 * (t >> 5) + 8 * ((t & 15) >> 2) + 4 * ((t >> 4) & 1) + (t & 3);
 }
 
-template <int DT, int D>
+// W waves per workgroup: 4, or 8 at D = 128 for long prompts (registers
+// allow two waves per SIMD either way there, so one eight-wave workgroup
+// stages each K/V tile for 256 query rows where two four-wave workgroups
+// staged it for 128 each: half the staging work and L2 traffic per row; on
+// short prompts the larger ranges cost more at the causal diagonal than that
+// saves).
+template <int DT, int D, int W>
 struct PfTile {
-  // waves per workgroup: eight at D = 128, where registers allow two per
-  // SIMD either way: one workgroup then stages each K/V tile for 256 query
-  // rows instead of two workgroups staging it for 128 each (half the L2
-  // traffic and staging work)
-  static constexpr int kWaves = D == 128 ? 8 : 4;
+  static constexpr int kWaves = W;
   static constexpr int kTiles = 2;                 // 16-row query tiles per wave
   static constexpr int kRows = 16 * kTiles * kWaves;  // query tokens per workgroup
   static constexpr int kKvTile = 64;               // K/V tokens per LDS tile
@@ -112,14 +115,14 @@ struct PfTile {
   static_assert(kVUnits <= kWaves * 64, "one V unit per thread at most");
 };
 
-template <int DT, int D, int G>
-__global__ __launch_bounds__((PfTile<DT, D>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(2)))
+template <int DT, int D, int G, int W>
+__global__ __launch_bounds__((PfTile<DT, D, W>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
                     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
                     const int32_t* __restrict__ slots, const int32_t* __restrict__ cu_seqlens,
                     PfShape sh) {
-  using T = PfTile<DT, D>;
+  using T = PfTile<DT, D, W>;
   using Mth = PfMath<DT>;
   using E = Elem<DT>;
   constexpr int NKS = T::NKS, NE = T::NE, RH = T::RH;
@@ -361,28 +364,41 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   }
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, int W>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
-  using T = PfTile<DT, D>;
+  using T = PfTile<DT, D, W>;
   PfShape sh{a.num_q_heads, a.num_kv_heads, a.num_blocks,
              (a.max_seqlen + T::kRows - 1) / T::kRows, a.num_tokens, a.scale_log2};
   dim3 grid((unsigned)sh.query_tiles, (unsigned)a.num_q_heads, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((prefill_kernel<DT, D, G>), grid, dim3(T::kWaves * 64), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<DT, D, G, W>), grid, dim3(T::kWaves * 64), 0, stream,
                      (uint16_t*)a.out, (const uint16_t*)a.q, (const uint16_t*)a.key,
                      (const uint16_t*)a.value, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache,
                      a.slot_mapping, a.cu_seqlens, sh);
   return hipGetLastError();
 }
 
-template <int DT, int D>
-hipError_t launch_prefill_group(const PrefillArgs& a, int group, hipStream_t stream) {
+// Eight waves at D = 128 from this prompt length on (Llama-7B shape, 4096
+// tokens: 0.345 -> 0.351-0.358 of peak; Qwen3 shape, 1024 tokens: 604 ->
+// 621-633 us with eight).
+constexpr int kPfLongPrompt = 2048;
+
+template <int DT, int D, int W>
+hipError_t launch_prefill_waves(const PrefillArgs& a, int group, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_prefill_typed<DT, D, 1>(a, stream);
-    case 2: return launch_prefill_typed<DT, D, 2>(a, stream);
-    case 4: return launch_prefill_typed<DT, D, 4>(a, stream);
-    case 8: return launch_prefill_typed<DT, D, 8>(a, stream);
+    case 1: return launch_prefill_typed<DT, D, 1, W>(a, stream);
+    case 2: return launch_prefill_typed<DT, D, 2, W>(a, stream);
+    case 4: return launch_prefill_typed<DT, D, 4, W>(a, stream);
+    case 8: return launch_prefill_typed<DT, D, 8, W>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int DT, int D>
+hipError_t launch_prefill_group(const PrefillArgs& a, int group, hipStream_t stream) {
+  if constexpr (D == 128) {
+    if (a.max_seqlen >= kPfLongPrompt) return launch_prefill_waves<DT, D, 8>(a, group, stream);
+  }
+  return launch_prefill_waves<DT, D, 4>(a, group, stream);
 }
 
 }  // namespace

@@ -48,6 +48,22 @@ def test_sweep_dtype_headdim_group(dtype, d, g):
     check(pf)
 
 
+@pytest.mark.parametrize("dtype,hq", [("bf16", 8), ("f16", 2)])
+def test_long_batch_with_ragged_prompts(dtype, hq):
+    """head_dim 128 with a prompt of 2048 tokens or more takes eight-wave
+    workgroups (256-token query ranges): a ragged batch around those ranges'
+    edges, with empty and one-token prompts, every row against the oracle and
+    the pools bit-exact."""
+    lens = [2100, 0, 1, 255, 256, 257, 511, 300]
+    pf = W.make_prefill(dtype, lens, hq, 2, 128, seed=12 + hq)
+    before_k, before_v = bits(pf.k_cache), bits(pf.v_cache)
+    g, _ = check(pf)
+    k_ref, v_ref = oracle.cache_write(before_k, before_v, bits(pf.key), bits(pf.value),
+                                      pf.slot_mapping.numpy())
+    assert np.array_equal(bits(g.k_cache), k_ref)
+    assert np.array_equal(bits(g.v_cache), v_ref)
+
+
 def test_cache_write_is_bit_exact():
     """The pools after the call equal the oracle's write of every row into its
     slot (a negative slot is skipped), everything else untouched."""
