@@ -9,17 +9,16 @@
 // over the prompt's tokens 0..t, and every token's K/V row goes to the slot
 // the block manager gave it (same page, "2. 分页KV缓存（PagedAttention）").
 //
-// Work decomposition: one workgroup of W waves (4, or 8 at head_dim 128 for
-// prompts of 2048 tokens or more) per
-// (32 W query tokens, query head, prompt). Wave w owns two 16-row tiles, query tokens [16w, 16w +
-// 16) and [16W + 16w, 16W + 16w + 16) of the workgroup's range, so the waves reach
-// the causal diagonal at similar depths. The workgroup walks the prompt's K/V
-// rows from token 0 to its last query token in 64-token tiles, double
-// buffered in LDS: the next tile's global loads are in flight while the
-// current one is computed, and one barrier per tile separates the two. The
-// K/V rows come from the new key/value tensors (contiguous per prompt), not
-// through the block table: they are this pass's own rows. Later query ranges
-// carry more work and are dispatched first.
+// Work decomposition: one workgroup of W = 4 waves per (32 W query tokens,
+// query head, prompt). Wave w owns two 16-row tiles, query tokens [16w,
+// 16w + 16) and [16W + 16w, 16W + 16w + 16) of the workgroup's range, so the
+// waves reach the causal diagonal at similar depths. The workgroup walks the
+// prompt's K/V rows from token 0 to its last query token in 64-token tiles,
+// double buffered in LDS: the next tile streams from memory straight into
+// LDS while the current one is computed, and one barrier per tile separates
+// the two. The K/V rows come from the new key/value tensors (contiguous per
+// prompt), not through the block table: they are this pass's own rows.
+// Later query ranges carry more work and are dispatched first.
 //
 // Per 32 K/V tokens a wave runs, for each of its tiles:
 //   S^T = K Q^T     two v_mfma_f32_16x16x32 chains (16 tokens x 16 rows each);
@@ -31,17 +30,16 @@
 //                   index. The 8 p values a lane holds are exactly its
 //                   A-operand slots once the reduction index is ordered
 //                   (tokens 4*q4..4*q4+3, then 16+4*q4..16+4*q4+3) for lane
-//                   group q4; V is stored transposed in LDS in that token
-//                   order, so each B operand is one 16-byte LDS read.
+//                   group q4; each B operand (those 8 tokens of one V
+//                   column) comes from two transposed LDS reads
+//                   (ds_read_b64_tr_b16) of the row-major V tile.
 //   l += P 1        one more MFMA against a ones operand sums the same rounded
 //                   p per row, in the output's own layout.
 // The K/V fragments a wave reads from LDS serve both of its tiles.
 //
-// LDS: the K tile is row-major with rows padded to D + 16 elements and the
-// transposed V tile has rows of kVtPitch = 80 elements. With these pitches the
-// operand reads and the staging writes measure free of bank conflicts
-// (SQ_LDS_BANK_CONFLICT = 0); pitches of D + 8 and 72 cost 0.64 conflict cycles
-// per conflict-free LDS cycle, D and 64 cost 1.9.
+// LDS: K and V tiles are row-major, loaded straight from the prompt's rows
+// (buffer loads to LDS), with the 16-byte chunks of each row permuted (swz_k,
+// swz_v) so that the operand reads meet no bank conflicts.
 #include "attention_mfma.h"
 #include "device_common.h"
 #include "launch.h"
@@ -54,6 +52,7 @@ namespace {
 typedef __bf16 pf_bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 pf_f16x2_t __attribute__((ext_vector_type(2)));
 typedef float pf_f32x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 template <int DT> struct PfMath;
 template <> struct PfMath<0> {  // binary16
@@ -82,51 +81,68 @@ struct PfShape {
   float scale_log2;
 };
 
-// Position of token t of a tile in a transposed-V row: inside each
-// 32-token half, lane group q4 reads positions 8*q4 .. 8*q4+7, which hold
-// tokens 4*q4..4*q4+3 and 16+4*q4..16+4*q4+3.
-__device__ __forceinline__ int vt_pos(int t) {
-  return 32 * (t >> 5) + 8 * ((t & 15) >> 2) + 4 * ((t >> 4) & 1) + (t & 3);
-}
 
-// W waves per workgroup: 4, or 8 at D = 128 for long prompts (registers
-// allow two waves per SIMD either way there, so one eight-wave workgroup
-// stages each K/V tile for 256 query rows where two four-wave workgroups
-// staged it for 128 each: half the staging work and L2 traffic per row; on
-// short prompts the larger ranges cost more at the causal diagonal than that
-// saves).
-template <int DT, int D, int W>
+template <int DT, int D>
 struct PfTile {
-  static constexpr int kWaves = W;
+  static constexpr int kWaves = 4;                 // waves per workgroup
   static constexpr int kTiles = 2;                 // 16-row query tiles per wave
   static constexpr int kRows = 16 * kTiles * kWaves;  // query tokens per workgroup
   static constexpr int kKvTile = 64;               // K/V tokens per LDS tile
-  static constexpr int kVtPitch = kKvTile + 16;    // transposed-V row pitch, elements
   static constexpr int NKS = D / 32;               // QK reduction steps of 32
   static constexpr int NE = D / 16;                // PV output column groups
   static constexpr int kChunks = D / 8;            // 16-byte chunks per row
-  static constexpr int RH = D + 16;                // K tile pitch, elements
-  static constexpr int kKPerThread = kKvTile * kChunks / (kWaves * 64);
-  static constexpr int kVUnits = (kKvTile / 4) * kChunks;  // (4 tokens x 1 chunk) units
-  static constexpr int kKBytes = kKvTile * RH * 2;
-  static constexpr int kVBytes = D * kVtPitch * 2;
-  static constexpr int kBufBytes = kKBytes + kVBytes;
-  static_assert(kKPerThread * kWaves * 64 == kKvTile * kChunks, "K tile split");
-  static_assert(kVUnits <= kWaves * 64, "one V unit per thread at most");
+  static constexpr int kTileBytes = kKvTile * D * 2;  // one K or V tile, row-major
+  static constexpr int kBufBytes = 2 * kTileBytes;    // K tile, then V tile
+  // 1 KB LDS-DMA loads (64 lanes x 16 bytes) per wave for one K or V tile
+  static constexpr int kDmaPerWave = kKvTile * kChunks / 64 / kWaves;
+  static_assert(kDmaPerWave * kWaves * 64 == kKvTile * kChunks, "tile split into 1 KB loads");
 };
 
-template <int DT, int D, int G, int W>
-__global__ __launch_bounds__((PfTile<DT, D, W>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(2)))
+// gfx950 LDS instructions, wrapped in plain device functions (called from
+// the kernel template, a direct builtin call would also have to instantiate
+// in the host compilation, which lacks these target features):
+// 16 bytes per lane from a buffer straight into LDS (lane l writes bytes
+// 16 l .. 16 l + 15 after `lds`), and a transposed 16-bit read (lane n of
+// each 16-lane group gets element n % 4 of the 8-byte reads of lanes
+// 4 k + n / 4, k = 0..3).
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Chunk swizzles of the row-major K and V tiles (16-byte chunk c of row r
+// sits at chunk position c ^ swz(r) of its row), chosen so that the operand
+// reads use every LDS bank once per cycle: a K operand read takes one chunk
+// of 16 consecutive rows; a V transposed read takes two adjacent chunks of 8
+// consecutive rows. 256-byte rows (D = 128) start on the same bank, so the
+// swizzle alone separates them; 128-byte rows (D = 64) alternate between two
+// bank halves, so rows of one parity are separated.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__((PfTile<DT, D>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
                     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
                     const int32_t* __restrict__ slots, const int32_t* __restrict__ cu_seqlens,
                     PfShape sh) {
-  using T = PfTile<DT, D, W>;
+  using T = PfTile<DT, D>;
   using Mth = PfMath<DT>;
   using E = Elem<DT>;
-  constexpr int NKS = T::NKS, NE = T::NE, RH = T::RH;
-  constexpr int kPfKvTile = T::kKvTile, kVtPitch = T::kVtPitch;
+  constexpr int NKS = T::NKS, NE = T::NE, KC = T::kChunks;
+  constexpr int kPfKvTile = T::kKvTile;
   constexpr int kPfWaves = T::kWaves, kPfRows = T::kRows, NT = T::kTiles;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::kBufBytes];
 
@@ -197,74 +213,39 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   }
   const uint4 ones = make_uint4(Mth::kOnes, Mth::kOnes, Mth::kOnes, Mth::kOnes);
 
-  // Staging: K chunk u of this thread is (token idx / kChunks, chunk idx %
-  // kChunks), idx = tid + 256 u; the V unit is tokens 4*vg..4*vg+3 of chunk vc
-  // (token group fastest across lanes, so the transposed writes hit distinct
-  // banks).
-  constexpr int kVGroups = kPfKvTile / 4;
-  const int vg = tid % kVGroups;
-  const int vc = tid / kVGroups;
-  const bool v_owner = vc < T::kChunks;
-  uint4 kreg[T::kKPerThread];
-  uint4 vreg[4];
-  // The prompt's K/V rows through buffer descriptors that end at row q_end:
-  // rows past it read as zero (they are masked anyway), with no branches.
+  // Staging: the K and V tiles go from the prompt's rows straight into LDS
+  // (buffer loads to LDS, 1 KB per instruction, lane l filling bytes 16 l ..
+  // 16 l + 15 of it), so no registers hold a tile in flight. Lane l of load i
+  // fills chunk position p = 64 i + l of the tile: row p / KC, chunk
+  // (p % KC) ^ swz(row) of that token's row. The buffer descriptors end at
+  // row q_end: rows past it (the tail of the last tile) read as zero.
   const uint32_t row_stride = (uint32_t)Hkv * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(key + (size_t)lo * Hkv * D, (uint32_t)q_end * row_stride);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(value + (size_t)lo * Hkv * D, (uint32_t)q_end * row_stride);
   const uint32_t head_off = (uint32_t)h * D * 2;
-  auto fetch = [&](int kt0) {
-#pragma unroll
-    for (int u = 0; u < T::kKPerThread; ++u) {
-      const int idx = tid + kPfWaves * 64 * u;
-      const uint32_t t = kt0 + idx / T::kChunks;
-      kreg[u] = buffer_load16(krs, t * row_stride + head_off + 16u * (idx % T::kChunks));
-    }
-    if (v_owner) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t t = kt0 + 4 * vg + r;
-        vreg[r] = buffer_load16(vrs, t * row_stride + head_off + 16u * vc);
-      }
-    }
-  };
-  auto store = [&](int buf) {
+  auto fetch = [&](int buf, int kt0) {
     char* base = smem + buf * T::kBufBytes;
-    uint16_t* sk = (uint16_t*)base;
 #pragma unroll
-    for (int u = 0; u < T::kKPerThread; ++u) {
-      const int idx = tid + kPfWaves * 64 * u;
-      *(uint4*)(sk + (idx / T::kChunks) * RH + 8 * (idx % T::kChunks)) = kreg[u];
-    }
-    if (v_owner) {
-      uint16_t* svt = (uint16_t*)(base + T::kKBytes);
-      const int p = vt_pos(4 * vg);
-      const uint32_t* w0 = (const uint32_t*)&vreg[0];
-      const uint32_t* w1 = (const uint32_t*)&vreg[1];
-      const uint32_t* w2 = (const uint32_t*)&vreg[2];
-      const uint32_t* w3 = (const uint32_t*)&vreg[3];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {  // elements 2k and 2k+1 of the chunk
-        *(uint2*)(svt + (8 * vc + 2 * k) * kVtPitch + p) =
-            make_uint2(__builtin_amdgcn_perm(w1[k], w0[k], kPermLoHalves),
-                       __builtin_amdgcn_perm(w3[k], w2[k], kPermLoHalves));
-        *(uint2*)(svt + (8 * vc + 2 * k + 1) * kVtPitch + p) =
-            make_uint2(__builtin_amdgcn_perm(w1[k], w0[k], kPermHiHalves),
-                       __builtin_amdgcn_perm(w3[k], w2[k], kPermHiHalves));
-      }
+    for (int i = 0; i < T::kDmaPerWave; ++i) {
+      const int gi = wave * T::kDmaPerWave + i;  // this wave's i-th 1 KB piece of a tile
+      const int p = 64 * gi + lane;
+      const int row = p / KC, pos = p % KC;
+      const uint32_t trow = (uint32_t)(kt0 + row) * row_stride + head_off;
+      load_to_lds16(krs, base + 1024 * gi, trow + 16u * (pos ^ swz_k<D>(row)));
+      load_to_lds16(vrs, base + T::kTileBytes + 1024 * gi, trow + 16u * (pos ^ swz_v<D>(row)));
     }
   };
 
   const int ntiles = (q_end + kPfKvTile - 1) / kPfKvTile;
-  fetch(0);
-  store(0);
-  __syncthreads();
+  fetch(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have reached LDS
+  lds_barrier();
   for (int kt = 0; kt < ntiles; ++kt) {
-    const bool more = kt + 1 < ntiles;
-    if (more) fetch((kt + 1) * kPfKvTile);  // in flight during the compute
-    const char* base = smem + (kt & 1) * T::kBufBytes;
-    const char* sk = base;
-    const char* svt = base + T::kKBytes;
+    // the next tile streams into the other buffer (read by every wave before
+    // the last barrier) while this one is computed
+    if (kt + 1 < ntiles) fetch((kt + 1) & 1, (kt + 1) * kPfKvTile);
+    const char* sk = smem + (kt & 1) * T::kBufBytes;
+    const char* sv = sk + T::kTileBytes;
 #pragma unroll
     for (int half = 0; half < kPfKvTile / 32; ++half) {  // 32 tokens at a time
       const int tok0 = kt * kPfKvTile + 32 * half;
@@ -282,13 +263,21 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            kf[b][ks] = *(const uint4*)(sk + (32 * half + 16 * b + r16) * (RH * 2) + 64 * ks +
-                                        16 * q4);
+            const int row = 32 * half + 16 * b + r16;
+            kf[b][ks] = *(const uint4*)(sk + 16 * (row * KC + ((4 * ks + q4) ^ swz_k<D>(row))));
           }
         }
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-          vf[e] = *(const uint4*)(svt + ((16 * e + r16) * kVtPitch + 32 * half + 8 * q4) * 2);
+          // two transposed reads: lane j of a 16-lane group reads 4 columns
+          // (16 e + 4 (j % 4) ...) of token row t0 + j / 4; the hardware hands
+          // lane n column 16 e + n of the four rows, so slots 0-3 hold tokens
+          // 4 q4 .. 4 q4 + 3 and slots 4-7 tokens 16 + 4 q4 .. 16 + 4 q4 + 3
+          const int t0 = 32 * half + 4 * q4 + ((lane & 15) >> 2);
+          const int c = 2 * e + ((lane & 3) >> 1);
+          const int off = 16 * (t0 * KC + (c ^ swz_v<D>(t0))) + 8 * (lane & 1);
+          const uint2 a = lds_read_tr16(sv + off), b = lds_read_tr16(sv + off + 16 * 16 * KC);
+          vf[e] = make_uint4(a.x, a.y, b.x, b.y);
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -344,8 +333,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         }
       }
     }
-    if (more) store((kt + 1) & 1);  // the other buffer is free since the last barrier
-    __syncthreads();  // the next tile is in LDS; this one may be overwritten
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile are in LDS
+    lds_barrier();
   }
 
   // Output rows rb[t] + 4*q4 + i, columns 16e + r16: divided by the row's sum.
@@ -364,41 +353,28 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   }
 }
 
-template <int DT, int D, int G, int W>
+template <int DT, int D, int G>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
-  using T = PfTile<DT, D, W>;
+  using T = PfTile<DT, D>;
   PfShape sh{a.num_q_heads, a.num_kv_heads, a.num_blocks,
              (a.max_seqlen + T::kRows - 1) / T::kRows, a.num_tokens, a.scale_log2};
   dim3 grid((unsigned)sh.query_tiles, (unsigned)a.num_q_heads, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((prefill_kernel<DT, D, G, W>), grid, dim3(T::kWaves * 64), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<DT, D, G>), grid, dim3(T::kWaves * 64), 0, stream,
                      (uint16_t*)a.out, (const uint16_t*)a.q, (const uint16_t*)a.key,
                      (const uint16_t*)a.value, (uint16_t*)a.k_cache, (uint16_t*)a.v_cache,
                      a.slot_mapping, a.cu_seqlens, sh);
   return hipGetLastError();
 }
 
-// Eight waves at D = 128 from this prompt length on (Llama-7B shape, 4096
-// tokens: 0.345 -> 0.351-0.358 of peak; Qwen3 shape, 1024 tokens: 604 ->
-// 621-633 us with eight).
-constexpr int kPfLongPrompt = 2048;
-
-template <int DT, int D, int W>
-hipError_t launch_prefill_waves(const PrefillArgs& a, int group, hipStream_t stream) {
-  switch (group) {
-    case 1: return launch_prefill_typed<DT, D, 1, W>(a, stream);
-    case 2: return launch_prefill_typed<DT, D, 2, W>(a, stream);
-    case 4: return launch_prefill_typed<DT, D, 4, W>(a, stream);
-    case 8: return launch_prefill_typed<DT, D, 8, W>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 template <int DT, int D>
 hipError_t launch_prefill_group(const PrefillArgs& a, int group, hipStream_t stream) {
-  if constexpr (D == 128) {
-    if (a.max_seqlen >= kPfLongPrompt) return launch_prefill_waves<DT, D, 8>(a, group, stream);
+  switch (group) {
+    case 1: return launch_prefill_typed<DT, D, 1>(a, stream);
+    case 2: return launch_prefill_typed<DT, D, 2>(a, stream);
+    case 4: return launch_prefill_typed<DT, D, 4>(a, stream);
+    case 8: return launch_prefill_typed<DT, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
   }
-  return launch_prefill_waves<DT, D, 4>(a, group, stream);
 }
 
 }  // namespace

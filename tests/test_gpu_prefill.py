@@ -50,10 +50,9 @@ def test_sweep_dtype_headdim_group(dtype, d, g):
 
 @pytest.mark.parametrize("dtype,hq", [("bf16", 8), ("f16", 2)])
 def test_long_batch_with_ragged_prompts(dtype, hq):
-    """head_dim 128 with a prompt of 2048 tokens or more takes eight-wave
-    workgroups (256-token query ranges): a ragged batch around those ranges'
-    edges, with empty and one-token prompts, every row against the oracle and
-    the pools bit-exact."""
+    """head_dim 128, one prompt of 2100 tokens among short ones around the
+    64-token tiles and 128-token query ranges, with empty and one-token
+    prompts: every row against the oracle and the pools bit-exact."""
     lens = [2100, 0, 1, 255, 256, 257, 511, 300]
     pf = W.make_prefill(dtype, lens, hq, 2, 128, seed=12 + hq)
     before_k, before_v = bits(pf.k_cache), bits(pf.v_cache)
