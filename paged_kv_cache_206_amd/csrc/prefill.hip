@@ -131,8 +131,12 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
+// Four waves per SIMD at head_dim 64 (128 VGPRs: TinyLlama shape 6.09 ->
+// 5.75 ms for 256 x 2048 tokens; its quarter-rate exponentials make it the
+// VALU-bound shape, and more resident waves hide more of the step's chain);
+// two at 128.
 template <int DT, int D, int G>
-__global__ __launch_bounds__((PfTile<DT, D>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((PfTile<DT, D>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
                     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
