@@ -2,7 +2,8 @@
 
 Each case draws its dtype, head_dim, GQA group, KV heads, batch, lengths
 (empty, one-token, block-edge and ragged ones mixed), partition length and,
-for decode, whether the cache write is fused, from a seed of its own; all
+for decode, whether the cache write is fused (and, for the planned call,
+where each new row goes), from a seed of its own; all
 inputs are valid. Tolerance as elsewhere: max |gpu - oracle| <= 2e-3 (fp16)
 / 1.5e-2 (bf16); pools after a write are compared bit for bit."""
 import numpy as np
@@ -12,7 +13,7 @@ import torch
 import oracle
 import paged_kv_cache_206_amd as mvk
 import workloads as W
-from gpu_helpers import TOL, bits, max_err
+from gpu_helpers import TOL, bits, max_err, oracle_decode_all
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +74,60 @@ def test_random_decode(case):
     assert max_err(out, ref, dtype) <= TOL[dtype]
     assert np.array_equal(bits(gl.k_cache), kc_ref)
     assert np.array_equal(bits(gl.v_cache), vc_ref)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_planned_decode(case):
+    """The planned call (a plan, then the layer's call) on random batches
+    within its scope: up to 300 sequences, contexts up to 7000 tokens (items
+    needing several descriptors of blocks), and with the fused write new rows
+    mostly at the newest position, some at an earlier position of the
+    sequence's own context, in a block nobody reads, or nowhere (-1)."""
+    rng = np.random.default_rng(5000 + case)
+    dtype, d, g, hkv = draw_shape(rng)
+    n = int(rng.integers(1, 31)) if rng.random() < 0.7 else int(rng.integers(200, 301))
+    lens = draw_lens(rng, n, [80, 700, 2500, 7000][case % 4])
+    fused = bool(rng.random() < 0.6)
+    free = int(rng.integers(2, 9))
+    nb = sum(-(-L // 16) for L in lens) + free
+    wl = W.make_custom("r", dtype, lens, g * hkv, hkv, d, nb, 6000 + case)
+    maxlen = max(lens)
+    assert mvk.plan_size(len(lens), g * hkv, hkv, d, maxlen) is not None
+    slots = wl.slot_mapping.clone()
+    if fused:
+        used = set(int(x) for x in wl.used_block_ids())
+        free_rows = [b * 16 + r for b in range(nb) if b not in used for r in range(16)]
+        rng.shuffle(free_rows)
+        for s_ in range(len(lens)):
+            r = rng.random()
+            L = lens[s_]
+            if r < 0.12 and L >= 2:              # an earlier token of its own context
+                t = int(rng.integers(0, L - 1))
+                slots[s_] = int(wl.block_tables[s_, t // 16]) * 16 + t % 16
+            elif r < 0.2 and free_rows:           # a block nobody reads
+                slots[s_] = free_rows.pop()
+            elif r < 0.27:
+                slots[s_] = -1
+    print(f"case {case}: {dtype} d={d} g={g} hkv={hkv} S={len(lens)} max L={maxlen} "
+          f"fused={fused}", flush=True)
+    layer = wl.layers[0]
+    kc, vc = bits(layer.k_cache), bits(layer.v_cache)
+    if fused:
+        kc, vc = oracle.cache_write(kc, vc, bits(layer.key), bits(layer.value), slots.numpy())
+    ref = oracle_decode_all(bits(layer.q), kc, vc, wl.block_tables.numpy(),
+                            wl.context_lens.numpy(), wl.scale, dtype)
+    gw = wl.to("cuda")
+    gl = gw.layers[0]
+    sm = slots.cuda()
+    plan = mvk.make_plan(gw.block_tables, gw.context_lens, g * hkv, hkv, d, maxlen,
+                         slot_mapping=sm if fused else None)
+    extra = dict(new_key=gl.key, new_value=gl.value) if fused else {}
+    out = mvk.paged_attention_decode_planned(gl.q, gl.k_cache, gl.v_cache, plan, gw.scale,
+                                             maxlen, **extra)
+    torch.cuda.synchronize()
+    assert max_err(out, ref, dtype) <= TOL[dtype]
+    assert np.array_equal(bits(gl.k_cache), kc)
+    assert np.array_equal(bits(gl.v_cache), vc)
 
 
 @pytest.mark.parametrize("case", range(12))
