@@ -38,8 +38,9 @@
 // The K/V fragments a wave reads from LDS serve both of its tiles.
 //
 // LDS: K and V tiles are row-major, loaded straight from the prompt's rows
-// (buffer loads to LDS), with the 16-byte chunks of each row permuted (swz_k,
-// swz_v) so that the operand reads meet no bank conflicts.
+// (buffer loads to LDS), with the 16-byte chunks of each row permuted (swz)
+// so that the operand reads meet no bank conflicts; the two tile buffers are
+// separate arrays (see the main loop).
 #include "attention_mfma.h"
 #include "device_common.h"
 #include "launch.h"
@@ -115,20 +116,23 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// Chunk swizzles of the row-major K and V tiles (16-byte chunk c of row r
+// Chunk swizzle of the row-major K and V tiles (16-byte chunk c of row r
 // sits at chunk position c ^ swz(r) of its row), chosen so that the operand
 // reads use every LDS bank once per cycle: a K operand read takes one chunk
 // of 16 consecutive rows; a V transposed read takes two adjacent chunks of 8
-// consecutive rows. 256-byte rows (D = 128) start on the same bank, so the
-// swizzle alone separates them; 128-byte rows (D = 64) alternate between two
-// bank halves, so rows of one parity are separated.
+// consecutive rows (rows 0-7 or 8-15 of a 16-row group). 256-byte rows
+// (D = 128) start on the same bank, so the swizzle alone separates them;
+// 128-byte rows (D = 64) alternate between two bank halves, so only rows of
+// one parity need separating (u = r / 2). With h = KC / 2, the low bits of u
+// pick an even chunk offset 2 (u % h) (two adjacent chunks of 8 rows land on
+// distinct pairs) and bit log2(h) of u the odd one (16 rows of one chunk land
+// on distinct positions). One swizzle for K and V lets both tiles' loads share
+// their per-lane offsets; the pattern repeats every 16 rows.
 template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-  return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+__device__ __forceinline__ int swz(int r) {
+  constexpr int kHalf = D / 16;
+  const int u = D == 128 ? r : (r >> 1);
+  return ((u & (kHalf - 1)) << 1) | ((u / kHalf) & 1);
 }
 
 // Four waves per SIMD at head_dim 64 (128 VGPRs: TinyLlama shape 6.09 ->
@@ -148,7 +152,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   constexpr int NKS = T::NKS, NE = T::NE, KC = T::kChunks;
   constexpr int kPfKvTile = T::kKvTile;
   constexpr int kPfWaves = T::kWaves, kPfRows = T::kRows, NT = T::kTiles;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::kBufBytes];
+  __shared__ __attribute__((aligned(16))) char smem0[T::kBufBytes];
+  __shared__ __attribute__((aligned(16))) char smem1[T::kBufBytes];
 
   // Workgroups are dealt round-robin to the XCDs in dispatch order; remap so
   // that each XCD runs whole (query head, prompt) groups. Their query ranges
@@ -207,6 +212,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
   }
   f32x4_t acc[NT][NE], lacc[NT];
+  // m: row r16's reference maximum (scaled, base 2)
   float m[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -221,123 +227,178 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   // (buffer loads to LDS, 1 KB per instruction, lane l filling bytes 16 l ..
   // 16 l + 15 of it), so no registers hold a tile in flight. Lane l of load i
   // fills chunk position p = 64 i + l of the tile: row p / KC, chunk
-  // (p % KC) ^ swz(row) of that token's row. The buffer descriptors end at
-  // row q_end: rows past it (the tail of the last tile) read as zero.
+  // (p % KC) ^ swz(row) of that token's row. Each tile's descriptors start at
+  // its first row and end at row q_end: rows past it (the tail of the last
+  // tile) read as zero, and the per-lane offsets are the same for every tile.
   const uint32_t row_stride = (uint32_t)Hkv * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(key + (size_t)lo * Hkv * D, (uint32_t)q_end * row_stride);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(value + (size_t)lo * Hkv * D, (uint32_t)q_end * row_stride);
-  const uint32_t head_off = (uint32_t)h * D * 2;
-  auto fetch = [&](int buf, int kt0) {
-    char* base = smem + buf * T::kBufBytes;
+  const uint16_t* kbase = key + (size_t)lo * Hkv * D;
+  const uint16_t* vbase = value + (size_t)lo * Hkv * D;
+  uint32_t off_dma[T::kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < T::kDmaPerWave; ++i) {
+    const int p = 64 * (wave * T::kDmaPerWave + i) + lane;
+    const int row = p / KC, pos = p % KC;
+    const uint32_t trow = (uint32_t)row * row_stride + (uint32_t)h * D * 2;
+    off_dma[i] = trow + 16u * (pos ^ swz<D>(row));
+  }
+  auto fetch = [&](char* base, int kt0) __attribute__((always_inline)) {
+    const uint32_t skip = (uint32_t)kt0 * row_stride;
+    const uint32_t bytes = (uint32_t)q_end * row_stride - skip;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char*)kbase + skip, bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char*)vbase + skip, bytes);
 #pragma unroll
     for (int i = 0; i < T::kDmaPerWave; ++i) {
       const int gi = wave * T::kDmaPerWave + i;  // this wave's i-th 1 KB piece of a tile
-      const int p = 64 * gi + lane;
-      const int row = p / KC, pos = p % KC;
-      const uint32_t trow = (uint32_t)(kt0 + row) * row_stride + head_off;
-      load_to_lds16(krs, base + 1024 * gi, trow + 16u * (pos ^ swz_k<D>(row)));
-      load_to_lds16(vrs, base + T::kTileBytes + 1024 * gi, trow + 16u * (pos ^ swz_v<D>(row)));
+      load_to_lds16(krs, base + 1024 * gi, off_dma[i]);
+      load_to_lds16(vrs, base + T::kTileBytes + 1024 * gi, off_dma[i]);
     }
   };
 
-  const int ntiles = (q_end + kPfKvTile - 1) / kPfKvTile;
-  fetch(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have reached LDS
-  lds_barrier();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    // the next tile streams into the other buffer (read by every wave before
-    // the last barrier) while this one is computed
-    if (kt + 1 < ntiles) fetch((kt + 1) & 1, (kt + 1) * kPfKvTile);
-    const char* sk = smem + (kt & 1) * T::kBufBytes;
+  // Per-lane byte offsets of the operand reads within a K or V tile, the
+  // same for both buffers and every 32-token half (the swizzle repeats every
+  // 16 rows)
+  int kofs[NKS], vofs[NE];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    kofs[ks] = 16 * (r16 * KC + ((4 * ks + q4) ^ swz<D>(r16)));
+    asm volatile("" : "+v"(kofs[ks]));
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int t0 = 4 * q4 + ((lane & 15) >> 2);
+    const int c = 2 * e + ((lane & 3) >> 1);
+    vofs[e] = 16 * (t0 * KC + (c ^ swz<D>(t0))) + 8 * (lane & 1);
+    asm volatile("" : "+v"(vofs[e]));
+  }
+
+  // Reads of one 32-token half of a K/V tile: the K fragments of its two
+  // 16-token blocks and the V fragments of its 32 tokens
+  auto read_frags = [&](const char* sk, const int hoff, uint4 (&kf)[2][NKS], uint4 (&vf)[NE])
+      __attribute__((always_inline)) {
     const char* sv = sk + T::kTileBytes;
 #pragma unroll
-    for (int half = 0; half < kPfKvTile / 32; ++half) {  // 32 tokens at a time
-      const int tok0 = kt * kPfKvTile + 32 * half;
-      bool act[NT];
-      bool any = false;
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        act[t] = rb[t] < n && tok0 <= rb[t] + 15;
-        any = any || act[t];
-      }
-      if (any) {  // uniform over the wave
-        // K fragments of the two 16-token blocks, V fragments of the 32 tokens
-        uint4 kf[2][NKS], vf[NE];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            const int row = 32 * half + 16 * b + r16;
-            kf[b][ks] = *(const uint4*)(sk + 16 * (row * KC + ((4 * ks + q4) ^ swz_k<D>(row))));
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          // two transposed reads: lane j of a 16-lane group reads 4 columns
-          // (16 e + 4 (j % 4) ...) of token row t0 + j / 4; the hardware hands
-          // lane n column 16 e + n of the four rows, so slots 0-3 hold tokens
-          // 4 q4 .. 4 q4 + 3 and slots 4-7 tokens 16 + 4 q4 .. 16 + 4 q4 + 3
-          const int t0 = 32 * half + 4 * q4 + ((lane & 15) >> 2);
-          const int c = 2 * e + ((lane & 3) >> 1);
-          const int off = 16 * (t0 * KC + (c ^ swz_v<D>(t0))) + 8 * (lane & 1);
-          const uint2 a = lds_read_tr16(sv + off), b = lds_read_tr16(sv + off + 16 * 16 * KC);
-          vf[e] = make_uint4(a.x, a.y, b.x, b.y);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (!act[t]) continue;
-          f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            s0 = Mth::mma(kf[0][ks], qop[t][ks], s0);
-            s1 = Mth::mma(kf[1][ks], qop[t][ks], s1);
-          }
-          float z[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            z[i] = s0[i];
-            z[4 + i] = s1[i];
-          }
-          if (tok0 + 31 > rb[t]) {  // the 32 tokens cross this tile's diagonal
-            const int lim = rb[t] + r16 + 1;  // row r16 sees tokens below lim
-            const int tb = tok0 + 4 * q4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (tb + i >= lim) z[i] = -INFINITY;
-              if (tb + 16 + i >= lim) z[4 + i] = -INFINITY;
-            }
-          }
-          const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), z[2]),
-                                 fmaxf(fmaxf(fmaxf(z[3], z[4]), z[5]), fmaxf(z[6], z[7]))) * sl2;
-          if (__any(mx > m[t] + kLazyRescale)) {
-            // the 4 lanes of a row (l, l^16, l^32, l^48) agree on its new reference
-            float bm = fmaxf(mx, __shfl_xor(mx, 16));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
-            const float mnew = bm > m[t] + kLazyRescale ? bm : m[t];
-            const float alpha = fast_exp2(m[t] - mnew);
-            m[t] = mnew;
-            // output rows 4*q4+i take the factor of the lane that holds row 4*q4+i
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float a = __shfl(alpha, 4 * q4 + i);
-              lacc[t][i] *= a;
-#pragma unroll
-              for (int e = 0; e < NE; ++e) acc[t][e][i] *= a;
-            }
-          }
-          const float nm = -m[t];
-          float p[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(z[i], sl2, nm));
-          const uint4 pa = make_uint4(Mth::pack(p[0], p[1]), Mth::pack(p[2], p[3]),
-                                      Mth::pack(p[4], p[5]), Mth::pack(p[6], p[7]));
-#pragma unroll
-          for (int e = 0; e < NE; ++e) acc[t][e] = Mth::mma(pa, vf[e], acc[t][e]);
-          lacc[t] = Mth::mma(pa, ones, lacc[t]);
-        }
-      }
+      for (int ks = 0; ks < NKS; ++ks)
+        kf[b][ks] = *(const uint4*)(sk + kofs[ks] + 16 * KC * (hoff + 16 * b));
     }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      // two transposed reads: lane j of a 16-lane group reads 4 columns
+      // (16 e + 4 (j % 4) ...) of token row t0 + j / 4; the hardware hands
+      // lane n column 16 e + n of the four rows, so slots 0-3 hold tokens
+      // 4 q4 .. 4 q4 + 3 and slots 4-7 tokens 16 + 4 q4 .. 16 + 4 q4 + 3
+      const char* vp = sv + vofs[e] + 16 * KC * hoff;
+      const uint2 a = lds_read_tr16(vp), b = lds_read_tr16(vp + 16 * 16 * KC);
+      vf[e] = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  };
+  auto qk = [&](const uint4 (&kf)[2][NKS], int t, float (&z)[8]) __attribute__((always_inline)) {
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s0 = Mth::mma(kf[0][ks], qop[t][ks], s0);
+      s1 = Mth::mma(kf[1][ks], qop[t][ks], s1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = s0[i];
+      z[4 + i] = s1[i];
+    }
+  };
+  auto max8 = [](const float (&z)[8]) __attribute__((always_inline)) {
+    return fmaxf(fmaxf(fmaxf(fmaxf(z[0], z[1]), z[2]), fmaxf(fmaxf(z[3], z[4]), z[5])),
+                 fmaxf(z[6], z[7]));
+  };
+  // Raise tile t's reference to the row maximum where it passed the old one
+  // by more than kLazyRescale, scaling the row's sums by 2^(m_old - m_new)
+  auto rescale = [&](int t, float mx) __attribute__((always_inline)) {
+    // the 4 lanes of a row (l, l^16, l^32, l^48) agree on its new reference
+    float bm = mx * sl2;
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mnew = bm > m[t] + kLazyRescale ? bm : m[t];
+    const float alpha = fast_exp2(m[t] - mnew);
+    m[t] = mnew;
+    // output rows 4*q4+i take the factor of the lane that holds row 4*q4+i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = __shfl(alpha, 4 * q4 + i);
+      lacc[t][i] *= a;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc[t][e][i] *= a;
+    }
+  };
+  auto accumulate = [&](int t, const float (&z)[8], const uint4 (&vf)[NE]) __attribute__((always_inline)) {
+    const float nm = -m[t];
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(z[i], sl2, nm));
+    const uint4 pa = make_uint4(Mth::pack(p[0], p[1]), Mth::pack(p[2], p[3]),
+                                Mth::pack(p[4], p[5]), Mth::pack(p[6], p[7]));
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[t][e] = Mth::mma(pa, vf[e], acc[t][e]);
+    lacc[t] = Mth::mma(pa, ones, lacc[t]);
+  };
+
+  // One 32-token step of the K/V tile in buffer sk (tokens tok0 .., hoff
+  // into the tile): a tile wholly above the diagonal (or past the prompt's
+  // end) is skipped, and tokens past a row's own are masked where the step
+  // crosses a tile's diagonal.
+  auto step = [&](const char* sk, const int tok0, const int hoff) __attribute__((always_inline)) {
+    bool act[NT];
+    bool any = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      act[t] = rb[t] < n && tok0 <= rb[t] + 15;
+      any = any || act[t];
+    }
+    if (!any) return;  // uniform over the wave
+    uint4 kf[2][NKS], vf[NE];
+    read_frags(sk, hoff, kf, vf);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (!act[t]) continue;
+      float z[8];
+      qk(kf, t, z);
+      if (tok0 + 31 > rb[t]) {  // the 32 tokens cross this tile's diagonal
+        const int lim = rb[t] + r16 + 1;  // row r16 sees tokens below lim
+        const int tb = tok0 + 4 * q4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (tb + i >= lim) z[i] = -INFINITY;
+          if (tb + 16 + i >= lim) z[4 + i] = -INFINITY;
+        }
+      }
+      // raise the reference only where a scaled logit passes it by more than
+      // kLazyRescale (sl2 > 0, so the raw maximum scales to the scaled one)
+      const float mx = max8(z);
+      if (__any(__builtin_fmaf(mx, sl2, -m[t]) > kLazyRescale)) rescale(t, mx);
+      accumulate(t, z, vf);
+    }
+  };
+
+  // Two LDS buffers, used alternately: the next tile streams into one while
+  // the other is computed. They are separate arrays so that the compiler can
+  // tell the loads into one from the reads of the other (with one array it
+  // makes every read wait for all of this wave's loads, the next tile's
+  // included); the explicit wait for this wave's loads and the barrier after
+  // each tile order the rest.
+  const int ntiles = (q_end + kPfKvTile - 1) / kPfKvTile;
+  fetch(smem0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have reached LDS
+  lds_barrier();
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    if (kt + 1 < ntiles) fetch(smem1, (kt + 1) * kPfKvTile);
+    step(smem0, kt * kPfKvTile, 0);
+    step(smem0, kt * kPfKvTile + 32, 32);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile are in LDS
+    lds_barrier();
+    if (kt + 1 >= ntiles) break;
+    if (kt + 2 < ntiles) fetch(smem0, (kt + 2) * kPfKvTile);
+    step(smem1, (kt + 1) * kPfKvTile, 0);
+    step(smem1, (kt + 1) * kPfKvTile + 32, 32);
+    __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
   }
 
