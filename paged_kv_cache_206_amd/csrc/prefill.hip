@@ -212,16 +212,20 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
   }
   f32x4_t acc[NT][NE], lacc[NT];
-  // m: row r16's reference maximum (scaled, base 2)
-  float m[NT];
+  // nm: minus row r16's reference maximum (scaled, base 2), the addend of
+  // every exponent
+  float nm[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[t][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m[t] = kNegBig;
+    nm[t] = -kNegBig;
   }
-  const uint4 ones = make_uint4(Mth::kOnes, Mth::kOnes, Mth::kOnes, Mth::kOnes);
+  uint4 ones = make_uint4(Mth::kOnes, Mth::kOnes, Mth::kOnes, Mth::kOnes);
+  // kept in registers (as a known constant the compiler rebuilds it with
+  // three moves before every use)
+  asm volatile("" : "+v"(ones.x), "+v"(ones.y), "+v"(ones.z), "+v"(ones.w));
 
   // Staging: the K and V tiles go from the prompt's rows straight into LDS
   // (buffer loads to LDS, 1 KB per instruction, lane l filling bytes 16 l ..
@@ -317,9 +321,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     float bm = mx * sl2;
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mnew = bm > m[t] + kLazyRescale ? bm : m[t];
-    const float alpha = fast_exp2(m[t] - mnew);
-    m[t] = mnew;
+    const float mold = -nm[t];
+    const float mnew = bm > mold + kLazyRescale ? bm : mold;
+    const float alpha = fast_exp2(mold - mnew);
+    nm[t] = -mnew;
     // output rows 4*q4+i take the factor of the lane that holds row 4*q4+i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -330,10 +335,9 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
   };
   auto accumulate = [&](int t, const float (&z)[8], const uint4 (&vf)[NE]) __attribute__((always_inline)) {
-    const float nm = -m[t];
     float p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(z[i], sl2, nm));
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(z[i], sl2, nm[t]));
     const uint4 pa = make_uint4(Mth::pack(p[0], p[1]), Mth::pack(p[2], p[3]),
                                 Mth::pack(p[4], p[5]), Mth::pack(p[6], p[7]));
 #pragma unroll
@@ -362,18 +366,19 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
       float z[8];
       qk(kf, t, z);
       if (tok0 + 31 > rb[t]) {  // the 32 tokens cross this tile's diagonal
-        const int lim = rb[t] + r16 + 1;  // row r16 sees tokens below lim
-        const int tb = tok0 + 4 * q4;
+        // row r16 sees tokens up to its own: this lane's tokens tok0 + 4 q4 + i
+        // (+ 16) are visible while i (+ 16) < vis
+        const int vis = rb[t] + r16 + 1 - (tok0 + 4 * q4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (tb + i >= lim) z[i] = -INFINITY;
-          if (tb + 16 + i >= lim) z[4 + i] = -INFINITY;
+          if (i >= vis) z[i] = -INFINITY;
+          if (16 + i >= vis) z[4 + i] = -INFINITY;
         }
       }
       // raise the reference only where a scaled logit passes it by more than
       // kLazyRescale (sl2 > 0, so the raw maximum scales to the scaled one)
       const float mx = max8(z);
-      if (__any(__builtin_fmaf(mx, sl2, -m[t]) > kLazyRescale)) rescale(t, mx);
+      if (__any(__builtin_fmaf(mx, sl2, nm[t]) > kLazyRescale)) rescale(t, mx);
       accumulate(t, z, vf);
     }
   };
