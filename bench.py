@@ -541,7 +541,7 @@ def run_prefill(args, torch, mvk, W, wl, nlayers_step, dev):
     T = S * L
     step_s = per_call_us * nlayers_step / 1e6
     result = {
-        "metric": "paged-decode KV read GB/s (% of MI355X HBM peak); decode tokens/s",
+        "metric": "prefill attention TFLOP/s (causal, fused cache write; fraction of MI355X dense MFMA peak)",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -38,7 +38,8 @@
 // The K/V fragments a wave reads from LDS serve both of its tiles.
 //
 // LDS: K and V tiles are row-major, loaded straight from the prompt's rows
-// (buffer loads to LDS), with the 16-byte chunks of each row permuted (swz)
+// (buffer loads to LDS), with the 16-byte chunks of each row permuted (swz_k,
+// swz_v)
 // so that the operand reads meet no bank conflicts; the two tile buffers are
 // separate arrays (see the main loop).
 #include "attention_mfma.h"
@@ -116,29 +117,29 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// Chunk swizzle of the row-major K and V tiles (16-byte chunk c of row r
+// Chunk swizzles of the row-major K and V tiles (16-byte chunk c of row r
 // sits at chunk position c ^ swz(r) of its row), chosen so that the operand
-// reads use every LDS bank once per cycle: a K operand read takes one chunk
-// of 16 consecutive rows; a V transposed read takes two adjacent chunks of 8
-// consecutive rows (rows 0-7 or 8-15 of a 16-row group). 256-byte rows
-// (D = 128) start on the same bank, so the swizzle alone separates them;
-// 128-byte rows (D = 64) alternate between two bank halves, so only rows of
-// one parity need separating (u = r / 2). With h = KC / 2, the low bits of u
-// pick an even chunk offset 2 (u % h) (two adjacent chunks of 8 rows land on
-// distinct pairs) and bit log2(h) of u the odd one (16 rows of one chunk land
-// on distinct positions). One swizzle for K and V lets both tiles' loads share
-// their per-lane offsets; the pattern repeats every 16 rows.
+// reads meet no bank conflicts: a K operand read takes one chunk of 16
+// consecutive rows; a V transposed read takes two adjacent chunks of 8
+// consecutive rows. 256-byte rows (D = 128) start on the same bank, so the
+// swizzle alone separates them; 128-byte rows (D = 64) alternate between two
+// bank halves, so rows of one parity are separated. Both repeat every 16
+// rows. (A single swizzle meeting both patterns on paper, ((u % (KC/2)) << 1)
+// | bit log2(KC/2) of u with u the row, or the row / 2 at D = 64, measured
+// about one conflict cycle per two conflict-free ones on gfx950.)
 template <int D>
-__device__ __forceinline__ int swz(int r) {
-  constexpr int kHalf = D / 16;
-  const int u = D == 128 ? r : (r >> 1);
-  return ((u & (kHalf - 1)) << 1) | ((u / kHalf) & 1);
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
-// Four waves per SIMD at head_dim 64 (128 VGPRs: TinyLlama shape 6.09 ->
-// 5.75 ms for 256 x 2048 tokens; its quarter-rate exponentials make it the
-// VALU-bound shape, and more resident waves hide more of the step's chain);
-// two at 128.
+// Four waves per SIMD at head_dim 64 (at most 128 VGPRs; 122 used): its
+// exponentials make it the VALU-bound shape, and more resident waves hide
+// more of the step's chain (against three waves per SIMD, 6.09 -> 5.75 ms
+// for 256 x 2048 tokens when first measured); two at 128 (214 VGPRs).
 template <int DT, int D, int G>
 __global__ __launch_bounds__((PfTile<DT, D>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
@@ -237,13 +238,14 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const uint32_t row_stride = (uint32_t)Hkv * D * 2;
   const uint16_t* kbase = key + (size_t)lo * Hkv * D;
   const uint16_t* vbase = value + (size_t)lo * Hkv * D;
-  uint32_t off_dma[T::kDmaPerWave];
+  uint32_t koff_dma[T::kDmaPerWave], voff_dma[T::kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < T::kDmaPerWave; ++i) {
     const int p = 64 * (wave * T::kDmaPerWave + i) + lane;
     const int row = p / KC, pos = p % KC;
     const uint32_t trow = (uint32_t)row * row_stride + (uint32_t)h * D * 2;
-    off_dma[i] = trow + 16u * (pos ^ swz<D>(row));
+    koff_dma[i] = trow + 16u * (pos ^ swz_k<D>(row));
+    voff_dma[i] = trow + 16u * (pos ^ swz_v<D>(row));
   }
   auto fetch = [&](char* base, int kt0) __attribute__((always_inline)) {
     const uint32_t skip = (uint32_t)kt0 * row_stride;
@@ -253,8 +255,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < T::kDmaPerWave; ++i) {
       const int gi = wave * T::kDmaPerWave + i;  // this wave's i-th 1 KB piece of a tile
-      load_to_lds16(krs, base + 1024 * gi, off_dma[i]);
-      load_to_lds16(vrs, base + T::kTileBytes + 1024 * gi, off_dma[i]);
+      load_to_lds16(krs, base + 1024 * gi, koff_dma[i]);
+      load_to_lds16(vrs, base + T::kTileBytes + 1024 * gi, voff_dma[i]);
     }
   };
 
@@ -264,14 +266,14 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   int kofs[NKS], vofs[NE];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    kofs[ks] = 16 * (r16 * KC + ((4 * ks + q4) ^ swz<D>(r16)));
+    kofs[ks] = 16 * (r16 * KC + ((4 * ks + q4) ^ swz_k<D>(r16)));
     asm volatile("" : "+v"(kofs[ks]));
   }
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const int t0 = 4 * q4 + ((lane & 15) >> 2);
     const int c = 2 * e + ((lane & 3) >> 1);
-    vofs[e] = 16 * (t0 * KC + (c ^ swz<D>(t0))) + 8 * (lane & 1);
+    vofs[e] = 16 * (t0 * KC + (c ^ swz_v<D>(t0))) + 8 * (lane & 1);
     asm volatile("" : "+v"(vofs[e]));
   }
 
