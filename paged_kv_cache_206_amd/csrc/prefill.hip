@@ -39,9 +39,8 @@
 //
 // LDS: K and V tiles are row-major, loaded straight from the prompt's rows
 // (buffer loads to LDS), with the 16-byte chunks of each row permuted (swz_k,
-// swz_v)
-// so that the operand reads meet no bank conflicts; the two tile buffers are
-// separate arrays (see the main loop).
+// swz_v) so that the operand reads meet no bank conflicts; the two tile
+// buffers are separate arrays (see the main loop).
 #include "attention_mfma.h"
 #include "device_common.h"
 #include "launch.h"
@@ -49,7 +48,6 @@
 namespace mvk {
 
 namespace {
-
 
 typedef __bf16 pf_bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 pf_f16x2_t __attribute__((ext_vector_type(2)));
@@ -118,10 +116,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
 }
 
 // Chunk swizzles of the row-major K and V tiles (16-byte chunk c of row r
-// sits at chunk position c ^ swz(r) of its row), chosen so that the operand
-// reads meet no bank conflicts: a K operand read takes one chunk of 16
-// consecutive rows; a V transposed read takes two adjacent chunks of 8
-// consecutive rows. 256-byte rows (D = 128) start on the same bank, so the
+// sits at chunk position c ^ swz_k(r) of its row in K, c ^ swz_v(r) in V),
+// chosen so that the operand reads meet no bank conflicts: a K operand read
+// takes one chunk of 16 consecutive rows; a V transposed read takes two
+// adjacent chunks of 8 consecutive rows. 256-byte rows (D = 128) start on the same bank, so the
 // swizzle alone separates them; 128-byte rows (D = 64) alternate between two
 // bank halves, so rows of one parity are separated. Both repeat every 16
 // rows. (A single swizzle meeting both patterns on paper, ((u % (KC/2)) << 1)
@@ -232,7 +230,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   // (buffer loads to LDS, 1 KB per instruction, lane l filling bytes 16 l ..
   // 16 l + 15 of it), so no registers hold a tile in flight. Lane l of load i
   // fills chunk position p = 64 i + l of the tile: row p / KC, chunk
-  // (p % KC) ^ swz(row) of that token's row. Each tile's descriptors start at
+  // (p % KC) ^ swz_k(row) (swz_v for V) of that token's row. Each tile's descriptors start at
   // its first row and end at row q_end: rows past it (the tail of the last
   // tile) read as zero, and the per-lane offsets are the same for every tile.
   const uint32_t row_stride = (uint32_t)Hkv * D * 2;
@@ -261,8 +259,9 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   };
 
   // Per-lane byte offsets of the operand reads within a K or V tile, the
-  // same for both buffers and every 32-token half (the swizzle repeats every
-  // 16 rows)
+  // same for both buffers and every 32-token half (the swizzles repeat every
+  // 16 rows); kept opaque so that the compiler adds each buffer's address as
+  // an instruction offset instead of holding one register per buffer
   int kofs[NKS], vofs[NE];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
