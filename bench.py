@@ -76,7 +76,8 @@ def parse_args():
     ap.add_argument("--new-tokens", type=int, default=1, metavar="N",
                     help="new tokens per sequence; N > 1 runs the multi-query kernel")
     ap.add_argument("--no-plan", action="store_true",
-                    help="time the plain decode call even where the planned path applies")
+                    help="time the plain decode (or multi-query) call even where the planned "
+                         "path applies")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads' per-call lines in the default run")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -446,12 +447,28 @@ def run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt
                                                     args.partition)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(qq) for qq in queries]
+    # the planned call where the library covers the batch (a plan per step;
+    # one 16-row tile per (sequence, KV head): n * g <= 16)
+    planned = (not args.no_plan and args.partition == 0 and n_new * (Hq // Hkv) <= 16
+               and not (D == 128 and Hq == Hkv)
+               and mvk.plan_size(S, Hq, Hkv, D, maxlen) is not None)
+    plan = mvk.make_plan(bt, cl, Hq, Hkv, D, maxlen) if planned else None
 
-    def call(li):
+    def make_plan():
+        mvk.make_plan(bt, cl, Hq, Hkv, D, maxlen, plan=plan)
+
+    def call_unplanned(li):
         l = layers[li]
         mvk.paged_attention_multi_query(queries[li], l.k_cache, l.v_cache, bt, cl, qs, wl.scale,
                                         max_query_len=n_new, max_context_len=maxlen,
                                         out=outs[li], partition_tokens=part, workspace=ws)
+
+    def call(li):
+        if not planned:
+            return call_unplanned(li)
+        l = layers[li]
+        mvk.paged_attention_multi_query_planned(queries[li], l.k_cache, l.v_cache, plan, qs, S,
+                                                wl.scale, n_new, maxlen, out=outs[li])
 
     for _ in range(max(1, args.warmup)):
         for li in range(len(layers)):
@@ -461,7 +478,12 @@ def run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt
     # the step (all layers) captured once and replayed; per-call time from the same graph
     per_call_us = graph_time_per_call(torch, dev, [lambda li=li: call(li) for li in range(len(layers))],
                                       reps)
-    ms_per_step = per_call_us * nlayers_step / 1e3
+    plan_us = graph_time_per_call(torch, dev, [make_plan] * 8, reps) if planned else None
+    unplanned_us = None
+    if planned:   # the same calls without the plan, for reference
+        unplanned_us = graph_time_per_call(
+            torch, dev, [lambda li=li: call_unplanned(li) for li in range(len(layers))], reps)
+    ms_per_step = (per_call_us * nlayers_step + (plan_us or 0.0)) / 1e3
 
     lens = wl.context_lens.to(torch.int64)
     e = 2
@@ -479,7 +501,8 @@ def run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt
         "steps": reps * nsets,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "launch": "hipgraph replay of back-to-back multi-query calls",
+        "launch": "hipgraph replay of back-to-back multi-query calls"
+                  + (" (one plan per step, then every layer's planned call)" if planned else ""),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -491,21 +514,26 @@ def run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": 16, "layers_per_step": nlayers_step, "max_context_len": maxlen,
             "new_tokens": n_new, "partition_tokens": part, "pool_sets": nsets,
+            "planned": planned,
         },
         "pct_hbm_peak": round(100.0 * alg * nlayers_step / step_s / 1e9 / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(T / step_s, 1),
         "kv_bytes_per_step": kv_logical * nlayers_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_mq_partition_kernel",
+            "kernel": "paged_mq_planned_kernel" if planned else "paged_mq_partition_kernel",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload, False, kind=f"paged_multi_query_n{n_new}"),
+            "traffic": measured_traffic(args.workload, False,
+                                        kind=("paged_multi_query_planned_n" if planned else
+                                              "paged_multi_query_n") + str(n_new)),
             "alg_bytes_per_launch": alg,
             "launch_us": round(per_call_us, 3),
             "launch_us_method": "hipgraph of back-to-back multi-query calls, events around the replays",
+            "plan_us_per_step": None if plan_us is None else round(plan_us, 3),
+            "launch_us_unplanned": None if unplanned_us is None else round(unplanned_us, 3),
         },
     }
     if not args.no_cpu and args.cpu_seconds > 0:
@@ -618,6 +646,7 @@ def cpu_baseline_multi_query(wl, layers, queries, qs, budget_s, kv_logical_per_l
 KERNEL_SOURCES = {"paged_decode": "paged_decode.hip",
                   "paged_decode_planned": "paged_decode_planned.hip",
                   "paged_multi_query": "paged_multi_query.hip",
+                  "paged_multi_query_planned": "paged_multi_query.hip",
                   "prefill": "prefill.hip"}
 
 

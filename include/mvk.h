@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MVK_ABI_VERSION 6
+#define MVK_ABI_VERSION 7
 
 typedef enum mvk_status {
     MVK_OK = 0,
@@ -392,6 +392,44 @@ int32_t mvk_paged_attention_multi_query(void* out, const void* q,
                                         int32_t max_blocks_per_seq, int32_t max_context_len,
                                         float scale, int32_t dtype, int32_t partition_tokens,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mvk_paged_attention_multi_query_planned - the multi-query call through a
+ * step's plan (mvk_paged_attention_plan), for single-pass batches: the same
+ * definition and arithmetic as mvk_paged_attention_multi_query (the rows'
+ * summation order differs, so results may differ in the last bits; both are
+ * within the same bound of the exact result), with the (sequence, KV head)
+ * items dealt to workgroups by the plan instead of one workgroup per item.
+ * A speculative-verification step runs every layer over the same block
+ * tables, context lengths and query offsets, so the plan is built once per
+ * step as for decode
+ * ("从零手写 vLLM 核心：mini-vllm 项目深度解析", "推测解码原理" and
+ * "关键工程决策" items 1-3).
+ *   plan, plan_bytes  a plan built by mvk_paged_attention_plan from this
+ *                 call's block_tables and context_lens with slot_mapping =
+ *                 NULL, the same num_seqs, num_q_heads, num_kv_heads, head_dim
+ *                 and max_context_len (stream order). A plan built with new-
+ *                 token slots is a decode step's (its runs end before each
+ *                 sequence's last position): every output row of a sequence
+ *                 with a slot is then written as NaN.
+ *   out, q, k_cache, v_cache, query_start, num_query_tokens, max_query_len,
+ *   scale, dtype, block_size, num_blocks: as for mvk_paged_attention_multi_query.
+ * Scope: the plan's (mvk_paged_attention_plan_size), max_query_len * g <= 16,
+ * and not head_dim 128 with g = 1 (MVK_ERR_UNSUPPORTED otherwise;
+ * mvk_paged_attention_multi_query covers every batch). No workspace.
+ * num_seqs == 0 or num_query_tokens == 0 is a no-op. Repeated calls give
+ * identical bits. Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_UNSUPPORTED,
+ * MVK_ERR_WORKSPACE_TOO_SMALL (plan_bytes), MVK_ERR_HIP.
+ */
+int32_t mvk_paged_attention_multi_query_planned(void* out, const void* q, const void* k_cache,
+                                                const void* v_cache, const void* plan,
+                                                size_t plan_bytes, const int32_t* query_start,
+                                                int32_t num_seqs, int32_t num_query_tokens,
+                                                int32_t max_query_len, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t num_blocks,
+                                                int32_t max_context_len, float scale,
+                                                int32_t dtype, void* stream);
 
 /*
  * mvk_prefill_attention - causal self-attention of new prompts, with their

@@ -39,7 +39,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmvk.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 MVK_OK = 0
 MVK_ERR_INVALID_ARGUMENT = 1
 MVK_ERR_UNSUPPORTED = 2
@@ -91,6 +91,9 @@ SIGNATURES = {
         _c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _ptr, _c_size,
                  _ptr]),
+    "mvk_paged_attention_multi_query_planned": (
+        _c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _c_size, _ptr, _c_int, _c_int, _c_int, _c_int,
+                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _ptr]),
     "mvk_bm_create": (_ptr, [_c_int, _c_int, _c_int]),
     "mvk_bm_destroy": (None, [_ptr]),
     "mvk_bm_num_free": (_c_int, [_ptr]),
@@ -507,6 +510,39 @@ def paged_attention_multi_query(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
         _dtype_code(q), partition_tokens, ws_ptr, ws_bytes,
         _stream(q, out, k_cache, v_cache, block_tables, context_lens, query_start, workspace))
     _check("mvk_paged_attention_multi_query", st)
+    return out
+
+
+def paged_attention_multi_query_planned(q: torch.Tensor, k_cache: torch.Tensor,
+                                        v_cache: torch.Tensor, plan: torch.Tensor,
+                                        query_start: torch.Tensor, num_seqs: int, scale: float,
+                                        max_query_len: int, max_context_len: int,
+                                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """paged_attention_multi_query through a plan (make_plan of the same block
+    tables and context lengths, without slot_mapping): `num_seqs`,
+    `max_context_len` and the heads must be the plan's; `max_query_len`
+    bounds the new tokens per sequence."""
+    _require(q, "q", ndim=3)
+    _require(k_cache, "k_cache", dtype=q.dtype, ndim=4)
+    _require(v_cache, "v_cache", dtype=q.dtype, ndim=4)
+    _require(plan, "plan", dtype=torch.uint8)
+    _require(query_start, "query_start", dtype=torch.int32, ndim=1)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d or query_start.shape[0] != num_seqs + 1:
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", dtype=q.dtype)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    st = lib().mvk_paged_attention_multi_query_planned(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), plan.data_ptr(),
+        plan.numel(), query_start.data_ptr(), num_seqs, T, max_query_len, hq, hkv, d, bs, nb,
+        max_context_len, float(scale), _dtype_code(q),
+        _stream(q, out, k_cache, v_cache, plan, query_start))
+    _check("mvk_paged_attention_multi_query_planned", st)
     return out
 
 

@@ -676,6 +676,59 @@ int32_t mvk_paged_attention_multi_query(
   return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
 }
 
+int32_t mvk_paged_attention_multi_query_planned(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const void* plan,
+    size_t plan_bytes, const int32_t* query_start, int32_t num_seqs, int32_t num_query_tokens,
+    int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale, int32_t dtype,
+    void* stream) {
+  if (dtype != MVK_F16 && dtype != MVK_BF16) return MVK_ERR_INVALID_ARGUMENT;
+  if (block_size != kBlock) return MVK_ERR_UNSUPPORTED;
+  if (num_blocks <= 0 || !isfinite(scale)) return MVK_ERR_INVALID_ARGUMENT;
+  if (num_query_tokens < 0 || max_query_len < 1 || max_query_len > kMaxQueryLen)
+    return MVK_ERR_INVALID_ARGUMENT;
+  PlanGeom g{};
+  const int32_t st =
+      plan_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, &g);
+  if (st != MVK_OK) return st;
+  if ((int64_t)num_query_tokens > (int64_t)num_seqs * max_query_len)
+    return MVK_ERR_INVALID_ARGUMENT;
+  const int32_t group = num_q_heads / num_kv_heads;
+  // one 16-row MFMA tile per item; head_dim 128 with g = 1 runs four waves
+  // per SIMD in the plan's bins, too few registers for the tile
+  if (max_query_len * group > kMqRowTile || (head_dim == 128 && group == 1))
+    return MVK_ERR_UNSUPPORTED;
+  if (g.bins == 0 || num_query_tokens == 0) return MVK_OK;
+  if (!out || !q || !k_cache || !v_cache || !plan || !query_start) return MVK_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(plan) || !aligned4(query_start))
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (out == q || out == k_cache || out == v_cache || k_cache == v_cache)
+    return MVK_ERR_INVALID_ARGUMENT;
+  if (plan_bytes < g.bytes) return MVK_ERR_WORKSPACE_TOO_SMALL;
+  mvk::PlannedMultiQueryArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.plan = (const int32_t*)plan;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_query_tokens = num_query_tokens;
+  a.max_query_len = max_query_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.num_bins = g.bins;
+  a.desc_ints = g.desc_ints;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  a.dtype = dtype;
+  const hipError_t err = mvk::launch_paged_multi_query_planned(a, (hipStream_t)stream);
+  return err == hipSuccess ? MVK_OK : MVK_ERR_HIP;
+}
+
 int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const void* value,
                               void* k_cache, void* v_cache, const int32_t* slot_mapping,
                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_tokens,

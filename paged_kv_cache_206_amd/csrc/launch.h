@@ -73,6 +73,18 @@ constexpr int32_t kPlanMaxBlocks = kPlanDescInts - kPlanHdrInts;  // blocks per 
 constexpr int32_t kPlanMaxSeqs = 1024;   // sequences one plan ranks (in LDS)
 constexpr int32_t kPlanMaxKvHeads = 256;  // KV heads of a planned batch
 
+// Descriptor header fields (ints 0..7); the rest are the wave's block ids.
+enum : int {
+  kDescSeq = 0,       // sequence (negative: idle wave)
+  kDescHead = 1,      // KV head
+  kDescTokBegin = 2,  // first token of the wave's run (a multiple of 16)
+  kDescTokEnd = 3,    // one past its last token
+  kDescSlot = 4,      // the sequence's new-token slot (fused cache write), or -1
+  kDescWaves = 5,     // first wave of the item (bits 0-7), waves of the item (bits 8-15)
+  kDescLen = 6,       // the sequence's context length
+  kDescFlags = 7,     // the wave's part in the fused cache write
+};
+
 struct DecodePlanArgs {
   int32_t* plan;
   const int32_t* block_tables;
@@ -99,6 +111,25 @@ struct PlannedDecodeArgs {
 };
 
 hipError_t launch_paged_decode_planned(const PlannedDecodeArgs& a, hipStream_t stream);
+
+// Multi-query attention through a decode plan built without new-token slots
+// (single-pass batches, n * g <= 16 rows per item): every wave streams its
+// descriptor's blocks for all n * g query rows of its item.
+struct PlannedMultiQueryArgs {
+  void* out;                   // [T, Hq, D]
+  const void* q;               // [T, Hq, D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* plan;
+  const int32_t* query_start;  // [S + 1]
+  int32_t num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim;
+  int32_t num_blocks, max_context_len, num_bins;
+  int32_t desc_ints;           // the plan's descriptor size
+  float scale_log2;
+  int32_t dtype;
+};
+
+hipError_t launch_paged_multi_query_planned(const PlannedMultiQueryArgs& a, hipStream_t stream);
 
 struct MultiQueryArgs {
   void* out;                   // [T, Hq, D]

@@ -54,17 +54,7 @@ namespace mvk {
 
 namespace {
 
-// Descriptor fields (ints 0..7); the rest (24 or 56 ints) are block ids.
-enum : int {
-  kDescSeq = 0,       // sequence (negative: idle wave)
-  kDescHead = 1,      // KV head
-  kDescTokBegin = 2,  // first token of the wave's run (a multiple of 16)
-  kDescTokEnd = 3,    // one past its last token
-  kDescSlot = 4,      // the sequence's new-token slot (fused cache write), or -1
-  kDescWaves = 5,     // first wave of the item (bits 0-7), waves of the item (bits 8-15)
-  kDescLen = 6,       // the sequence's context length
-  kDescFlags = 7,     // the wave's part in the fused cache write (kFlag*)
-};
+// Descriptor fields: kDesc* (launch.h); the rest (24 or 56 ints) are block ids.
 
 // Parts in the fused cache write (descriptor int kDescFlags), set by the plan
 // per item: when the new slot is the sequence's position L-1 (a decode

@@ -49,10 +49,14 @@ struct MqShape {
 // Sequence s's query rows [first, first + n): query_start clamped to [0, T]
 // and n to max_query_len, so inconsistent offsets never index outside q, out
 // or the partial states.
+__device__ __forceinline__ void mq_rows(int qs0, int qs1, int num_query_tokens, int max_query_len,
+                                        int& first, int& n) {
+  first = min(max(qs0, 0), num_query_tokens);
+  const int last = min(max(qs1, first), num_query_tokens);
+  n = min(last - first, max_query_len);
+}
 __device__ __forceinline__ void mq_rows(int qs0, int qs1, const MqShape& sh, int& first, int& n) {
-  first = min(max(qs0, 0), sh.num_query_tokens);
-  const int last = min(max(qs1, first), sh.num_query_tokens);
-  n = min(last - first, sh.max_query_len);
+  mq_rows(qs0, qs1, sh.num_query_tokens, sh.max_query_len, first, n);
 }
 
 // A work item, from the XCD-contiguous item index: row group fastest, then
@@ -348,6 +352,216 @@ hipError_t launch_mq_group(const MultiQueryArgs& a, int group, hipStream_t strea
   }
 }
 
+// ------------------------------------------------------ planned multi-query
+// The same rows through a decode plan (paged_decode_planned.hip, one per
+// step, built from the step's block tables and context lengths without
+// new-token slots), for items of at most 16 query rows (n * g <= 16): the
+// plan deals the (sequence, KV head) items to bins of kPlanWaves waves with
+// equal block counts and gives every wave a descriptor (item, token run,
+// block ids). Each wave streams its blocks once for the n * g rows of its
+// item, one 16-row MFMA tile whose rows carry their own causal limits, and
+// the item's waves merge through LDS (log-sum-exp rule, waves in order).
+// (Items of up to 32 rows in two tiles measured no faster than the unplanned
+// kernel: 15.7 against 15.3 us for 12 new tokens on the Qwen3 shape.) A plan
+// built with new-token slots is a decode step's: it ends the run of a
+// sequence's last wave before the sequence's last position (that step
+// computes the token from its new row), so this kernel refuses it by writing
+// the item's rows as NaN.
+struct MqPlannedShape {
+  int32_t num_seqs, num_kv_heads, num_blocks, max_context_len, max_query_len, num_query_tokens;
+  int32_t desc_ints;
+  float scale_log2;
+};
+
+// The plan's bins assume the planned decode kernel's occupancy: two waves
+// per SIMD at head_dim 128 with g >= 2 (one bin per CU), four otherwise.
+template <int D, int G>
+constexpr int kMqPlannedWavesPerSimd = (D == 64 || G == 1) ? 4 : 2;
+
+// Merge of the N waves wb .. wb+N-1 of an item for its rows [0, nrow):
+// element (r, d) is sum_w o_w 2^(m_w - M) / sum_w l_w 2^(m_w - M), waves in
+// order, M their largest reference.
+template <int N, int G, int D, int DT>
+__device__ __forceinline__ void mq_merge_item(uint16_t* __restrict__ out,
+                                              const float (*sm_o)[kMqRows * D],
+                                              const float (*sm_m)[kMqRows],
+                                              const float (*sm_l)[kMqRows], int wb, int wave,
+                                              int lane, int first, int nrow, int h, int Hq,
+                                              bool refuse) {
+  using E = Elem<DT>;
+  for (int idx = (wave - wb) * 64 + lane; idx < nrow * D; idx += N * 64) {
+    const int rl = idx / D;
+    const int d = idx % D;
+    float m[N], l[N], o[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      m[n] = sm_m[wb + n][rl];
+      l[n] = sm_l[wb + n][rl];
+      o[n] = sm_o[wb + n][rl * D + d];
+    }
+    float mm = m[0];
+#pragma unroll
+    for (int n = 1; n < N; ++n) mm = fmaxf(mm, m[n]);
+    float lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const float fct = fast_exp2(m[n] - mm);
+      lsum = fmaf(l[n], fct, lsum);
+      acc = fmaf(o[n], fct, acc);
+    }
+    const float res =
+        refuse ? __builtin_nanf("") : lsum > 0.0f ? acc * __builtin_amdgcn_rcpf(lsum) : 0.0f;
+    out[mq_out_row<G>(first, rl, h, Hq) * D + d] = E::round(res);
+  }
+}
+
+template <int DT, int D, int G, int W, int NPF>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
+    kMqPlannedWavesPerSimd<D, G>))) void paged_mq_planned_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ plan, const int32_t* __restrict__ query_start,
+    MqPlannedShape sh) {
+  using Policy = MfmaPolicy<DT, D, kMqRows>;
+  __shared__ float sm_o[W][kMqRows * D];
+  __shared__ float sm_m[W][kMqRows];
+  __shared__ float sm_l[W][kMqRows];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  // lane k holds descriptor int k; every field is clamped into range, so an
+  // inconsistent plan gives wrong rows but no access outside the buffers
+  const int dv = lane < sh.desc_ints ? plan[((size_t)blockIdx.x * W + wave) * sh.desc_ints + lane] : -1;
+  const int s_raw = __builtin_amdgcn_readlane(dv, kDescSeq);
+  const int h_raw = __builtin_amdgcn_readlane(dv, kDescHead);
+  const bool active = s_raw >= 0 && s_raw < sh.num_seqs && h_raw >= 0 && h_raw < sh.num_kv_heads;
+  const int s = active ? s_raw : 0;
+  const int h = active ? h_raw : 0;
+  const int L = min(max(__builtin_amdgcn_readlane(dv, kDescLen), 0), sh.max_context_len);
+  const int tb = min(max(__builtin_amdgcn_readlane(dv, kDescTokBegin), 0), L) & ~(kBlockTokens - 1);
+  const int te = min(max(__builtin_amdgcn_readlane(dv, kDescTokEnd), tb), L);
+  const int nblk =
+      active ? min((te - tb + kBlockTokens - 1) / kBlockTokens, sh.desc_ints - kPlanHdrInts) : 0;
+  const int wv = __builtin_amdgcn_readlane(dv, kDescWaves);
+  const int wb = min(wv & 0xff, W - 1);
+  const int wn = min(max((wv >> 8) & 0xff, 1), W - wb);
+  const bool in_item = active && wave >= wb && wave < wb + wn;
+  const bool refuse = __builtin_amdgcn_readlane(dv, kDescSlot) >= 0;  // a plan with slots
+
+  const int Hq = sh.num_kv_heads * G;
+  const uint32_t row_bytes = (uint32_t)sh.num_kv_heads * D * 2u;
+  const size_t block_bytes = (size_t)row_bytes * kBlockTokens;
+  const char* kbase = (const char*)(k_cache + (size_t)h * D);
+  const char* vbase = (const char*)(v_cache + (size_t)h * D);
+  Policy pol;
+  pol.init_rows(nullptr, lane, row_bytes);  // lane layout, empty state
+  int first = 0, n_new = 0;
+  if (in_item) {
+    typename Policy::Frag f[NPF];
+    auto block_of = [&](int k) {
+      const int blk = __builtin_amdgcn_readlane(dv, kPlanHdrInts + min(k, max(nblk - 1, 0)));
+      return ((unsigned)blk < (unsigned)sh.num_blocks) ? blk : 0;
+    };
+    // rows of block k past te read as zero; steps past the last block load
+    // through an empty descriptor (zeros, no memory access)
+    auto load_block = [&](typename Policy::Frag& fr, int k) {
+      const bool real = k < nblk;
+      const int blk = block_of(k);
+      const int kk = min(k, max(nblk - 1, 0));
+      const int rows = min(kBlockTokens, te - (tb + kk * kBlockTokens));
+      const uint32_t extent = real ? (uint32_t)(rows - 1) * row_bytes + D * 2u : 0u;
+      const size_t o = (size_t)blk * block_bytes;
+      pol.template load<kStreamLoad>(fr, make_rsrc(kbase + o, extent),
+                                     make_rsrc(vbase + o, extent), row_bytes);
+    };
+    // The K/V stream starts first (it needs only the descriptor); the query
+    // rows need the sequence's query offsets, one more round trip.
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) load_block(f[j], j);
+    __builtin_amdgcn_sched_barrier(0);
+    mq_rows(query_start[s], query_start[s + 1], sh.num_query_tokens, sh.max_query_len, first,
+            n_new);
+    // row r = lane % 16 of the item (new token r / G, query head h*G + r % G)
+    // sees the tokens below L - n + r/G + 1
+    const int r = lane & 15;
+    const bool valid = r < n_new * G;
+    if (valid) {
+      const uint16_t* qr = q + mq_out_row<G>(first, r, h, Hq) * D;
+#pragma unroll
+      for (int ks = 0; ks < Policy::NKS; ++ks)
+        pol.qop[ks] = *(const uint4*)(qr + 32 * ks + 8 * pol.q4);
+    }
+    const int row_end = valid ? min(te, L - n_new + r / G + 1) : 0;
+    auto process = [&](typename Policy::Frag& fr, int tok0) {
+      pol.arrange(fr);
+      pol.step(fr, tok0, row_end, sh.scale_log2);
+    };
+    // as in the planned decode: groups of NPF blocks whose refills are all
+    // real, then the last one or two groups, which skip the steps and
+    // refills past nblk
+    int k = 0;
+    for (; k + 2 * NPF <= nblk; k += NPF) {
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        process(f[j], tb + (k + j) * kBlockTokens);
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(f[j], k + j + NPF);
+      }
+    }
+    for (; k < nblk; k += NPF) {
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        if (k + j < nblk) process(f[j], tb + (k + j) * kBlockTokens);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + j + NPF < nblk) load_block(f[j], k + j + NPF);
+      }
+    }
+    pol.to_lds(sm_m[wave], sm_l[wave], sm_o[wave]);
+  }
+  lds_barrier();  // every wave of the workgroup takes part
+  const int nrow = min(kMqRows, n_new * G);
+  if (!in_item || nrow <= 0) return;
+  switch (wn) {
+    case 1: mq_merge_item<1, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, first, nrow, h, Hq, refuse); break;
+    case 2: mq_merge_item<2, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, first, nrow, h, Hq, refuse); break;
+    case 3: mq_merge_item<3, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, first, nrow, h, Hq, refuse); break;
+    case 4: mq_merge_item<4, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, first, nrow, h, Hq, refuse); break;
+    case 5: mq_merge_item<5, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, first, nrow, h, Hq, refuse); break;
+    case 6: mq_merge_item<6, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, first, nrow, h, Hq, refuse); break;
+    case 7: mq_merge_item<7, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, first, nrow, h, Hq, refuse); break;
+    default: mq_merge_item<8, G, D, DT>(out, sm_o, sm_m, sm_l, wb, wave, lane, first, nrow, h, Hq, refuse); break;
+  }
+}
+
+// Blocks in flight per wave: three, the planned decode's choice for its MFMA tile.
+constexpr int kMqPlannedPrefetch = 3;
+
+template <int DT, int D, int G>
+hipError_t launch_mq_planned_typed(const PlannedMultiQueryArgs& a, hipStream_t stream) {
+  if constexpr (D == 128 && G == 1) {
+    return hipErrorInvalidValue;  // four waves per SIMD leave too few registers
+  } else {
+    MqPlannedShape sh{a.num_seqs,      a.num_kv_heads,     a.num_blocks, a.max_context_len,
+                      a.max_query_len, a.num_query_tokens, a.desc_ints,  a.scale_log2};
+    hipLaunchKernelGGL((paged_mq_planned_kernel<DT, D, G, kPlanWaves, kMqPlannedPrefetch>),
+                       dim3((unsigned)a.num_bins), dim3(kPlanWaves * 64), 0, stream,
+                       (uint16_t*)a.out, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                       (const uint16_t*)a.v_cache, a.plan, a.query_start, sh);
+    return hipGetLastError();
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_mq_planned_group(const PlannedMultiQueryArgs& a, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_mq_planned_typed<DT, D, 1>(a, stream);
+    case 2: return launch_mq_planned_typed<DT, D, 2>(a, stream);
+    case 4: return launch_mq_planned_typed<DT, D, 4>(a, stream);
+    case 8: return launch_mq_planned_typed<DT, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_paged_multi_query(const MultiQueryArgs& a, hipStream_t stream) {
@@ -358,6 +572,17 @@ hipError_t launch_paged_multi_query(const MultiQueryArgs& a, hipStream_t stream)
   }
   return a.head_dim == 64 ? launch_mq_group<1, 64>(a, group, stream)
                           : launch_mq_group<1, 128>(a, group, stream);
+}
+
+
+hipError_t launch_paged_multi_query_planned(const PlannedMultiQueryArgs& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  if (a.dtype == 0) {
+    return a.head_dim == 64 ? launch_mq_planned_group<0, 64>(a, group, stream)
+                            : launch_mq_planned_group<0, 128>(a, group, stream);
+  }
+  return a.head_dim == 64 ? launch_mq_planned_group<1, 64>(a, group, stream)
+                          : launch_mq_planned_group<1, 128>(a, group, stream);
 }
 
 }  // namespace mvk

@@ -36,6 +36,7 @@ def test_header_declares_the_boundary():
         "mvk_paged_attention_plan_size", "mvk_paged_attention_plan",
         "mvk_paged_attention_decode_planned",
         "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query",
+        "mvk_paged_attention_multi_query_planned",
         "mvk_prefill_attention",
         "mvk_bm_create", "mvk_bm_destroy", "mvk_bm_num_free", "mvk_bm_can_admit", "mvk_bm_admit",
         "mvk_bm_append", "mvk_bm_rollback", "mvk_bm_release", "mvk_bm_seq_info",
@@ -56,7 +57,7 @@ def test_single_hip_runtime_mapped(mvk):
 
 
 def test_version_and_status_strings(mvk):
-    assert mvk.abi_version() == 6
+    assert mvk.abi_version() == 7
     assert mvk.status_string(0) == "ok"
     assert "scratch" in mvk.status_string(6)
     assert mvk.status_string(3) == "workspace too small"
@@ -280,6 +281,36 @@ def test_planned_decode_validation(mvk, over, status):
 
 def test_planned_decode_empty_batch_is_noop(mvk):
     assert planned_call(mvk, S=0, out=None, q=None, plan=None) == 0
+
+
+def mq_planned_call(mvk, **over):
+    a = dict(out=FAKE, q=FAKE * 2, k=FAKE * 3, v=FAKE * 4, plan=FAKE * 9, pb=1 << 20, qs=FAKE * 7,
+             S=4, T=12, maxq=3, hq=4, hkv=2, d=64, bs=16, nb=32, maxlen=45, scale=0.125, dtype=0,
+             stream=None)
+    a.update(over)
+    return mvk.lib().mvk_paged_attention_multi_query_planned(
+        a["out"], a["q"], a["k"], a["v"], a["plan"], a["pb"], a["qs"], a["S"], a["T"], a["maxq"],
+        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["maxlen"], a["scale"], a["dtype"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=3), 1), (dict(bs=8), 2), (dict(nb=0), 1), (dict(scale=math.inf), 1),
+    (dict(maxq=0), 1), (dict(maxq=2000), 1), (dict(T=13), 1), (dict(T=-1), 1),
+    (dict(plan=None), 1), (dict(q=None), 1), (dict(qs=None), 1), (dict(qs=FAKE * 7 + 2), 1),
+    (dict(out=FAKE * 2), 1), (dict(v=FAKE * 3), 1), (dict(pb=1000), 3),
+    (dict(d=256), 2), (dict(S=4000, T=12), 2), (dict(maxlen=7200), 2),
+    (dict(hq=16, hkv=2, maxq=3, T=12), 2),          # 24 rows of a group of 8: two tiles
+    (dict(hq=2, hkv=2, d=128), 2),                   # head_dim 128 with g = 1
+    (dict(hq=16, hkv=2, maxq=2, T=8, pb=1000), 3),   # 16 rows (one tile) are in scope
+])
+def test_planned_multi_query_validation(mvk, over, status):
+    assert mq_planned_call(mvk, **over) == status
+
+
+def test_planned_multi_query_empty_is_noop(mvk):
+    assert mq_planned_call(mvk, S=0, T=0, out=None, q=None, plan=None, qs=None) == 0
+    assert mq_planned_call(mvk, T=0, out=None, q=None, plan=None, qs=None) == 0
 
 
 def test_library_partition_choice(mvk):

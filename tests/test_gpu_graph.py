@@ -148,6 +148,41 @@ def test_multi_query_graph_replay_matches_eager(partition_tokens):
                      [(eager, graphed)], f"mq p={partition_tokens}", check)
 
 
+def test_planned_multi_query_graph_replay_matches_eager():
+    """The step the benchmark captures for a planned multi-query batch: the
+    plan, then the planned call, replayed; every replay against eager and the
+    oracle."""
+    lens = [300, 41, 7, 1000, 96]
+    wl = W.make_custom("g", "bf16", lens, 16, 8, 128, sum(-(-L // 16) for L in lens) + 4, 34)
+    q, qs = W.make_queries(wl, [5, 3, 7, 2, 6], seed=35)
+    maxlen, maxq = wl.max_context_len, 7
+    lc = wl.layers[0]
+    ref = oracle.paged_multi_query(bits(q), bits(lc.k_cache), bits(lc.v_cache),
+                                   wl.block_tables.numpy(), wl.context_lens.numpy(), qs.numpy(),
+                                   wl.scale, wl.dtype)
+    wl, q, qs = wl.to("cuda"), q.to("cuda"), qs.to("cuda")
+    layer = wl.layers[0]
+    plan = mvk.make_plan(wl.block_tables, wl.context_lens, wl.num_q_heads, wl.num_kv_heads,
+                         wl.head_dim, maxlen)
+
+    def call(out):
+        mvk.make_plan(wl.block_tables, wl.context_lens, wl.num_q_heads, wl.num_kv_heads,
+                      wl.head_dim, maxlen, plan=plan)
+        mvk.paged_attention_multi_query_planned(q, layer.k_cache, layer.v_cache, plan, qs,
+                                                wl.num_seqs, wl.scale, maxq, maxlen, out=out)
+    eager = torch.empty_like(q)
+    call(eager)
+    torch.cuda.synchronize()
+    assert max_err(eager, ref, "bf16") <= TOL["bf16"]
+    graphed = torch.empty_like(q)
+
+    def check(rep):
+        err = max_err(graphed, ref, "bf16")
+        assert err <= TOL["bf16"], (rep, err)
+    replay_and_check(lambda: call(graphed), lambda: graphed.fill_(float("nan")),
+                     [(eager, graphed)], "planned mq", check)
+
+
 def test_prefill_graph_replay_matches_eager():
     pf = W.make_prefill("f16", [200, 17, 64, 129], 16, 2, 64, seed=33)
     maxlen = pf.max_seqlen
