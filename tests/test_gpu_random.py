@@ -156,6 +156,35 @@ def test_random_multi_query(case):
     assert max_err(out, ref, dtype) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_random_planned_multi_query(case):
+    """The multi-query call through a step's plan: shapes in its scope (not
+    head_dim 128 with g = 1), up to 16 rows per item, contexts up to 7000
+    tokens (short and long descriptors, items over several waves)."""
+    rng = np.random.default_rng(8000 + case)
+    dtype, d, g, hkv = draw_shape(rng)
+    if d == 128 and g == 1:
+        d = 64
+    lens = draw_lens(rng, int(rng.integers(1, 40)), int(rng.choice([120, 900, 7000])), lo=1)
+    news = [int(rng.integers(0, min(L, 16 // g) + 1)) for L in lens]
+    news[0] = max(news[0], 1)
+    nb = sum(-(-L // 16) for L in lens) + 3
+    wl = W.make_custom("r", dtype, lens, g * hkv, hkv, d, nb, 9000 + case)
+    q, qs = W.make_queries(wl, news, 9500 + case)
+    print(f"case {case}: {dtype} d={d} g={g} hkv={hkv} lens={lens} news={news}", flush=True)
+    layer = wl.layers[0]
+    ref = oracle.paged_multi_query(bits(q), bits(layer.k_cache), bits(layer.v_cache),
+                                   wl.block_tables.numpy(), wl.context_lens.numpy(), qs.numpy(),
+                                   wl.scale, dtype)
+    gw = wl.to("cuda")
+    plan = mvk.make_plan(gw.block_tables, gw.context_lens, g * hkv, hkv, d, max(lens))
+    out = mvk.paged_attention_multi_query_planned(q.to("cuda"), gw.layers[0].k_cache,
+                                                  gw.layers[0].v_cache, plan, qs.to("cuda"),
+                                                  len(lens), gw.scale, max(news), max(lens))
+    torch.cuda.synchronize()
+    assert max_err(out, ref, dtype) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("case", range(10))
 def test_random_prefill(case):
     rng = np.random.default_rng(6000 + case)
