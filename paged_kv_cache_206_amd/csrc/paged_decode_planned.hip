@@ -64,7 +64,7 @@ namespace {
 // completed (store first); otherwise the item's first wave stores it.
 enum : int { kFlagAppend = 1, kFlagStore = 2, kFlagStoreFirst = 4 };
 
-constexpr int kBinThreads = 256;
+constexpr int kBinThreads = 512;
 
 template <int D, int G>
 constexpr int kPlannedWavesPerSimd = (D == 64 || G == 1) ? 4 : 2;
@@ -257,6 +257,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
 struct BinShape {
   int32_t num_seqs, num_kv_heads, max_blocks, max_context_len, num_bins;
   int32_t desc_ints;  // kPlanShortDescInts or kPlanDescInts
+  // reciprocals rounded up, ceil(2^32 / d), for divisions as a multiply-high
+  // (exact for n / d while n * d < 2^32): d = num_kv_heads (0 when it is
+  // one, whose reciprocal does not fit in 32 bits) and d = the block ids a
+  // descriptor holds
+  uint32_t kv_rcp, ids_rcp;
 };
 static_assert((uint64_t)kPlanMaxSeqs * kPlanMaxKvHeads * kPlanMaxKvHeads < (1ull << 32),
               "the plan's multiply-high division needs i * num_kv_heads < 2^32");
@@ -274,6 +279,7 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
   __shared__ int32_t seq_of_rank[kPlanMaxSeqs];
   __shared__ int32_t hdr[W][kPlanHdrInts];
   __shared__ int32_t holds[W];  // the wave's blocks include its item's new slot (not at L-1)
+  static_assert(W * W <= 64 && kBinThreads >= 64, "one lane per spare-wave candidate in wave 0");
   const int t = threadIdx.x;
   const int S = ps.num_seqs;
   if (t < W) holds[t] = 0;
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
   }
   lds_barrier();
   // rank = number of larger keys (a permutation of 0..S-1). Sequence s gets
-  // P = 256 / S threads (at least one), each counting over its slice of the
+  // P = kBinThreads / S threads (at least one), each counting over its slice of the
   // keys four at a time; the slices' counts meet in LDS.
   {
     const int P = S <= kBinThreads ? kBinThreads / S : 1;
@@ -340,88 +346,103 @@ __global__ __launch_bounds__(kBinThreads) void paged_decode_plan_bins_kernel(
     }
   }
   lds_barrier();
-  if (t < W) {
-    // Every one of the first W threads assembles the bin (the same answer,
-    // in registers, with loops over the W possible item slots) and writes
-    // the header of wave t. Item slot k is round k's item, present when that
-    // round reaches this bin.
+  if (t < 64) {
+    // Wave 0 assembles the bin and lanes t < W write the header of wave t.
+    // Lane k < W looks up item slot k: round k's item, present when that
+    // round reaches this bin (the present slots are a prefix).
     const int N = S * ps.num_kv_heads;
     const int B = ps.num_bins;
     const int max_ids = ps.desc_ints - kPlanHdrInts;  // block ids a descriptor holds
     const int b = blockIdx.x;
-    // i / num_kv_heads as a multiply-high by the reciprocal rounded up,
-    // ceil(2^32 / hkv): exact while i * hkv < 2^32, which holds for
-    // i < kPlanMaxSeqs * kPlanMaxKvHeads (one head needs no division: its
-    // reciprocal does not fit in 32 bits)
+    // i / num_kv_heads as a multiply-high: exact, since i * hkv < 2^32 for
+    // i < kPlanMaxSeqs * kPlanMaxKvHeads
     const uint32_t hkv = (uint32_t)ps.num_kv_heads;
-    const uint32_t rcp = hkv > 1u ? 0xFFFFFFFFu / hkv + 1u : 0u;
-    int is[W], ih[W], inb[W], iw[W];
+    int s = 0, h = 0, nb = 0, w0 = 0;
+    {
+      const int i = t * B + ((t & 1) ? B - 1 - b : b);
+      if (t < W && t * B < N && i < N) {
+        const int r = hkv > 1u ? (int)__umulhi((uint32_t)i, ps.kv_rcp) : i;
+        s = seq_of_rank[r];
+        h = i - r * (int)hkv;
+        nb = nblk[s];
+        // every item gets the waves its descriptors need (at least one)
+        w0 = max(1, (int)__umulhi((uint32_t)(nb + max_ids - 1), ps.ids_rcp));
+      }
+    }
     int used = 0;
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-      const int i = k * B + ((k & 1) ? B - 1 - b : b);
-      const bool ok = k * B < N && i < N;
-      const int r = hkv > 1u ? (int)__umulhi((uint32_t)i, rcp) : i;
-      const int s = ok ? seq_of_rank[r] : 0;
-      is[k] = s;
-      ih[k] = ok ? i - r * (int)hkv : 0;
-      inb[k] = ok ? nblk[s] : 0;
-      // every item gets the waves its descriptors need (at least one)
-      iw[k] = ok ? max(1, (inb[k] + max_ids - 1) / max_ids) : 0;
-      used += iw[k];
+    for (int k = 0; k < W; ++k) used += __builtin_amdgcn_readlane(w0, k);
+    const int spare = W - used;  // the host sizes the bins so that used <= W
+    const int items = __popcll(__ballot(t < W && w0 > 0));  // the present slots, a prefix
+    // The spare waves go one at a time to the item whose waves carry the
+    // most blocks each (the first such item on ties). Item k's j-th spare
+    // wave would be taken at a load of nb_k / (w0_k + j) blocks per wave,
+    // which falls as j grows, so these steps take exactly the `spare`
+    // largest candidates (k, j), ordered by that load, then k, then j. Lane
+    // k * W + j holds candidate (k, j) and counts the larger ones among the
+    // items * spare candidates (at most 16: each item takes a wave). A load is
+    // compared as nb * (420 / waves): an exact integer, since every wave
+    // count a candidate has (1 .. W - 1) divides 420; the quotients are
+    // packed 9 bits each into one constant.
+    static_assert(W <= 8, "420 / waves covers wave counts up to 7");
+    constexpr uint64_t kPer420 = 420ull | 210ull << 9 | 140ull << 18 | 105ull << 27 |
+                                 84ull << 36 | 70ull << 45 | 60ull << 54;
+    const int kc = t / W, jc = t % W;
+    const int nbc = __shfl(nb, kc), w0c = __shfl(w0, kc);
+    const int den = min(max(w0c + jc, 1), 7);
+    const int per420 = (int)((kPer420 >> (9 * (den - 1))) & 511u);
+    const bool cand = w0c > 0 && jc < spare;
+    const int key = cand ? ((nbc * per420) << 6) | (63 - t) : -1;  // unique, larger = earlier
+    int above = 0;
+    for (int k2 = 0; k2 < items; ++k2) {
+      for (int j2 = 0; j2 < spare; ++j2) above += __builtin_amdgcn_readlane(key, k2 * W + j2) > key;
     }
-    // each spare wave goes to the item whose waves carry the most blocks
-    // (largest blocks / waves, compared by cross-multiplication; the first
-    // such item on ties)
-    for (; used < W; ++used) {
-      int best = 0;
-#pragma unroll
-      for (int k = 1; k < W; ++k) {
-        if (iw[k] > 0 && (iw[best] == 0 || inb[k] * iw[best] > inb[best] * iw[k])) best = k;
-      }
-#pragma unroll
-      for (int k = 0; k < W; ++k) iw[k] += (k == best) ? 1 : 0;
-    }
+    const uint64_t taken = __ballot(cand && above < spare);
+    // lane k < W: item k's wave count
+    const int iw = w0 + __popcll((taken >> ((t % W) * W)) & ((1ull << W) - 1));
     // wave t's item: items take consecutive waves in slot order
-    int wb = 0, item = -1;
+    int wb = 0, item = -1, is = 0, ih = 0, inb = 0, wn = 0;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-      const bool mine = item < 0 && iw[k] > 0 && t < wb + iw[k];
-      if (mine) item = k;
-      if (item < 0) wb += iw[k];
-    }
-    int* hw = hdr[t];
-    if (item < 0) {
-#pragma unroll
-      for (int k = 0; k < kPlanHdrInts; ++k) hw[k] = 0;
-      hw[kDescSeq] = -1;
-    } else {
-      int s = 0, h = 0, nb = 0, wn = 0;
-#pragma unroll
-      for (int k = 0; k < W; ++k) {
-        if (k == item) {
-          s = is[k];
-          h = ih[k];
-          nb = inb[k];
-          wn = iw[k];
-        }
+      const int iwk = __builtin_amdgcn_readlane(iw, k);
+      const int sk = __builtin_amdgcn_readlane(s, k);
+      const int hk = __builtin_amdgcn_readlane(h, k);
+      const int nbk = __builtin_amdgcn_readlane(nb, k);
+      const bool mine = item < 0 && iwk > 0 && t < wb + iwk;
+      if (mine) {
+        item = k;
+        is = sk;
+        ih = hk;
+        inb = nbk;
+        wn = iwk;
       }
-      const int x = t - wb;
-      const int b0 = x * nb / wn, b1 = (x + 1) * nb / wn;
-      const bool last = x == wn - 1;
-      const bool app = appends[s] != 0;
-      hw[kDescSeq] = s;
-      hw[kDescHead] = h;
-      hw[kDescTokBegin] = b0 * kBlockTokens;
-      // the append wave's blocks end before the new token
-      hw[kDescTokEnd] = min(b1 * kBlockTokens, lens[s] - (app && last ? 1 : 0));
-      hw[kDescSlot] = slot_of[s];
-      hw[kDescWaves] = wb | (wn << 8);
-      hw[kDescLen] = lens[s];
-      // provisional: the store-first holder, if any, is found below
-      hw[kDescFlags] = slot_of[s] < 0 ? 0
-                       : app ? (last ? kFlagAppend | kFlagStore : 0)
-                             : (x == 0 ? kFlagStore : 0);
+      if (item < 0) wb += iwk;
+    }
+    if (t < W) {
+      int* hw = hdr[t];
+      if (item < 0) {
+#pragma unroll
+        for (int k = 0; k < kPlanHdrInts; ++k) hw[k] = 0;
+        hw[kDescSeq] = -1;
+      } else {
+        const int x = t - wb;
+        const int b0 = (int)((uint32_t)(x * inb) / (uint32_t)wn);
+        const int b1 = (int)((uint32_t)((x + 1) * inb) / (uint32_t)wn);
+        const bool last = x == wn - 1;
+        const bool app = appends[is] != 0;
+        hw[kDescSeq] = is;
+        hw[kDescHead] = ih;
+        hw[kDescTokBegin] = b0 * kBlockTokens;
+        // the append wave's blocks end before the new token
+        hw[kDescTokEnd] = min(b1 * kBlockTokens, lens[is] - (app && last ? 1 : 0));
+        hw[kDescSlot] = slot_of[is];
+        hw[kDescWaves] = wb | (wn << 8);
+        hw[kDescLen] = lens[is];
+        // provisional: the store-first holder, if any, is found below
+        hw[kDescFlags] = slot_of[is] < 0 ? 0
+                         : app ? (last ? kFlagAppend | kFlagStore : 0)
+                               : (x == 0 ? kFlagStore : 0);
+      }
     }
   }
   lds_barrier();
@@ -502,8 +523,10 @@ hipError_t launch_planned_dim(const PlannedDecodeArgs& a, int group, hipStream_t
 }  // namespace
 
 hipError_t launch_decode_plan(const DecodePlanArgs& a, hipStream_t stream) {
+  const uint32_t hkv = (uint32_t)a.num_kv_heads;
+  const uint32_t ids = (uint32_t)(a.desc_ints - kPlanHdrInts);
   BinShape ps{a.num_seqs, a.num_kv_heads, a.max_blocks_per_seq, a.max_context_len, a.num_bins,
-              a.desc_ints};
+              a.desc_ints, hkv > 1u ? 0xFFFFFFFFu / hkv + 1u : 0u, 0xFFFFFFFFu / ids + 1u};
   hipLaunchKernelGGL((paged_decode_plan_bins_kernel<kPlanWaves>), dim3((unsigned)a.num_bins),
                      dim3(kBinThreads), 0, stream, a.plan, a.block_tables, a.context_lens,
                      a.slot_mapping, ps);
