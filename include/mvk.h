@@ -37,7 +37,8 @@
  *     Token t of sequence s lives in physical block block_tables[s][t / 16] at
  *     offset t % 16. A flat slot number is block * 16 + offset.
  *   - Device-side index contents (block ids, slots, lengths) are not checked on
- *     the host. The kernels never access memory outside the buffers described
+ *     the host (mvk_check_indices counts bad entries on the device, on
+ *     request). The kernels never access memory outside the buffers described
  *     by the size arguments: an out-of-range block id is read as block 0 and an
  *     out-of-range slot is not written; the affected output is then unspecified.
  */
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MVK_ABI_VERSION 7
+#define MVK_ABI_VERSION 8
 
 typedef enum mvk_status {
     MVK_OK = 0,
@@ -489,6 +490,31 @@ int32_t mvk_prefill_attention(void* out, const void* q, const void* key, const v
  */
 int32_t mvk_stream_read_probe(const void* src, size_t bytes, void* sink, int32_t workgroups,
                               void* stream);
+
+/*
+ * mvk_check_indices - debug check of a step's index arrays, the optional
+ * device-side check the calls above skip (they never read index contents for
+ * validation). One small kernel counts, asynchronously on `stream`:
+ *   counts[0]  context lengths outside [0, max_context_len];
+ *   counts[1]  block ids a call would read (entries j < ceil(L / 16) of row s,
+ *              L = context_lens[s] clamped to [0, min(max_context_len,
+ *              16 * max_blocks_per_seq)]) outside [0, num_blocks);
+ *   counts[2]  slots >= 16 * num_blocks (a negative slot means no write).
+ * Arguments (device pointers):
+ *   counts        int64 [3], 8-byte aligned; written by the kernel (no prior
+ *                 zeroing needed); read it after synchronising the stream.
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; context_lens int32
+ *                 [num_seqs] (both may be NULL when num_seqs == 0).
+ *   slot_mapping  int32 [num_slots] (NULL allowed when num_slots == 0).
+ *   num_blocks > 0 (the pool's blocks); max_context_len >= 0.
+ * Allocates nothing; reads only the entries described above.
+ * Errors: MVK_ERR_INVALID_ARGUMENT, MVK_ERR_HIP.
+ */
+int32_t mvk_check_indices(int64_t* counts, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                          const int32_t* slot_mapping, int32_t num_slots, int32_t num_blocks,
+                          void* stream);
 
 /*
  * Block manager (host side): which physical 16-token blocks each sequence

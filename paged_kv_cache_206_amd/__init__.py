@@ -39,7 +39,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmvk.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 MVK_OK = 0
 MVK_ERR_INVALID_ARGUMENT = 1
 MVK_ERR_UNSUPPORTED = 2
@@ -81,6 +81,8 @@ SIGNATURES = {
                                                     _c_int, _c_int, _c_int, _c_float, _c_int,
                                                     _ptr]),
     "mvk_stream_read_probe": (_c_int, [_ptr, _c_size, _ptr, _c_int, _ptr]),
+    "mvk_check_indices": (_c_int, [_ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _ptr, _c_int, _c_int,
+                                   _ptr]),
     "mvk_paged_attention_multi_query_workspace_size": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                  ctypes.POINTER(_c_size), ctypes.POINTER(_c_int)]),
@@ -441,6 +443,31 @@ def stream_read_probe(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None 
     st = lib().mvk_stream_read_probe(src.data_ptr(), n, sink.data_ptr(), sink.numel(),
                                      _stream(src, sink))
     _check("mvk_stream_read_probe", st)
+
+
+def check_indices(block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                  num_blocks: int, slot_mapping: torch.Tensor | None = None) -> dict:
+    """Debug check of a step's index arrays on the device (the attention and
+    cache-write calls never validate index contents): the number of context
+    lengths outside [0, max_context_len], of block ids a call would read
+    outside [0, num_blocks), and of slots past the pool (negative slots mean
+    no write). Synchronises the current stream to read the counts."""
+    _require(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _require(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    if block_tables.shape[0] != context_lens.shape[0]:
+        raise ValueError("inconsistent shapes")
+    if slot_mapping is not None:
+        _require(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    counts = torch.empty(3, dtype=torch.int64, device=context_lens.device)
+    st = lib().mvk_check_indices(
+        counts.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), context_lens.shape[0],
+        block_tables.shape[1], max_context_len,
+        None if slot_mapping is None else slot_mapping.data_ptr(),
+        0 if slot_mapping is None else slot_mapping.shape[0], num_blocks,
+        _stream(counts, block_tables, context_lens, slot_mapping))
+    _check("mvk_check_indices", st)
+    c = counts.tolist()
+    return {"context_lens": c[0], "block_ids": c[1], "slots": c[2]}
 
 
 def multi_query_workspace_size(num_seqs: int, num_query_tokens: int, max_query_len: int,

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
         "mvk_abi_version", "mvk_status_string", "mvk_reshape_and_cache",
         "mvk_paged_attention_workspace_size", "mvk_paged_attention_workspace_bytes",
         "mvk_paged_attention_decode", "mvk_paged_attention_decode_noalloc",
-        "mvk_paged_attention_scratch_limit", "mvk_stream_read_probe",
+        "mvk_paged_attention_scratch_limit", "mvk_stream_read_probe", "mvk_check_indices",
         "mvk_paged_attention_plan_size", "mvk_paged_attention_plan",
         "mvk_paged_attention_decode_planned",
         "mvk_paged_attention_multi_query_workspace_size", "mvk_paged_attention_multi_query",
@@ -57,7 +57,7 @@ def test_single_hip_runtime_mapped(mvk):
 
 
 def test_version_and_status_strings(mvk):
-    assert mvk.abi_version() == 7
+    assert mvk.abi_version() == 8
     assert mvk.status_string(0) == "ok"
     assert "scratch" in mvk.status_string(6)
     assert mvk.status_string(3) == "workspace too small"
@@ -426,6 +426,17 @@ def test_stream_probe_validation(mvk, over):
     a = dict(src=FAKE, nbytes=1 << 20, sink=FAKE * 2, wg=256)
     a.update(over)
     assert mvk.lib().mvk_stream_read_probe(a["src"], a["nbytes"], a["sink"], a["wg"], None) == 1
+
+
+@pytest.mark.parametrize("over", [
+    dict(counts=None), dict(counts=FAKE + 4), dict(S=-1), dict(T=-1), dict(maxlen=-1),
+    dict(nblocks=0), dict(bt=None), dict(cl=None), dict(mb=0), dict(bt=FAKE + 2),
+    dict(cl=FAKE + 1), dict(slots=None), dict(slots=FAKE + 2)])
+def test_check_indices_validation(mvk, over):
+    a = dict(counts=FAKE, bt=FAKE, cl=FAKE, S=4, mb=8, maxlen=100, slots=FAKE, T=4, nblocks=32)
+    a.update(over)
+    assert mvk.lib().mvk_check_indices(a["counts"], a["bt"], a["cl"], a["S"], a["mb"],
+                                       a["maxlen"], a["slots"], a["T"], a["nblocks"], None) == 1
 
 
 def test_tensors_on_different_devices_are_rejected(mvk):
