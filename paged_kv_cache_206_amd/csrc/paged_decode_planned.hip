@@ -79,33 +79,47 @@ struct PlannedShape {
 // only their LDS slots are read and every loop unrolls): element (j, d) of
 // the item's g x D outputs is sum_w o_w 2^(m_w - M) / sum_w l_w 2^(m_w - M),
 // waves in order, M their largest reference; the division is one reciprocal
-// of the denominator (the output is rounded to 16 bits).
+// of the denominator (the output is rounded to 16 bits). Lane x of the
+// item's waves takes elements x, x + 64 N, ...: with fewer than g D / 64
+// waves a lane has several, and all of their reads are issued before any is
+// combined, so the lane waits for LDS once instead of once per element.
 template <int N, int W, int G, int D, int DT>
 __device__ __forceinline__ void merge_item(uint16_t* __restrict__ out, const float (*sm_o)[G * D],
                                            const float (*sm_m)[G], const float (*sm_l)[G], int wb,
                                            int wave, int lane, int s, int h, int Hq) {
   using E = Elem<DT>;
-  for (int idx = (wave - wb) * 64 + lane; idx < G * D; idx += N * 64) {
+  constexpr int kPer = (G * D + N * 64 - 1) / (N * 64);  // elements per lane, at most
+  const int first = (wave - wb) * 64 + lane;
+  if ((wave - wb) * 64 >= G * D) return;  // a wave with no elements (uniform)
+  float m[kPer][N], l[kPer][N], o[kPer][N];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    // past the last element a lane reads the last one again and stores nothing
+    const int idx = min(first + e * N * 64, G * D - 1);
     const int j = idx / D;
-    float m[N], l[N], o[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      m[n] = sm_m[wb + n][j];
-      l[n] = sm_l[wb + n][j];
-      o[n] = sm_o[wb + n][idx];
+      m[e][n] = sm_m[wb + n][j];
+      l[e][n] = sm_l[wb + n][j];
+      o[e][n] = sm_o[wb + n][idx];
     }
-    float mm = m[0];
+  }
 #pragma unroll
-    for (int n = 1; n < N; ++n) mm = fmaxf(mm, m[n]);
+  for (int e = 0; e < kPer; ++e) {
+    const int idx = first + e * N * 64;
+    float mm = m[e][0];
+#pragma unroll
+    for (int n = 1; n < N; ++n) mm = fmaxf(mm, m[e][n]);
     float lsum = 0.0f, acc = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      const float fct = fast_exp2(m[n] - mm);
-      lsum = fmaf(l[n], fct, lsum);
-      acc = fmaf(o[n], fct, acc);
+      const float fct = fast_exp2(m[e][n] - mm);
+      lsum = fmaf(l[e][n], fct, lsum);
+      acc = fmaf(o[e][n], fct, acc);
     }
-    out[((size_t)s * Hq + (size_t)h * G) * D + idx] =
-        E::round(lsum > 0.0f ? acc * __builtin_amdgcn_rcpf(lsum) : 0.0f);
+    if (idx < G * D)
+      out[((size_t)s * Hq + (size_t)h * G) * D + idx] =
+          E::round(lsum > 0.0f ? acc * __builtin_amdgcn_rcpf(lsum) : 0.0f);
   }
 }
 
