@@ -65,7 +65,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library choice)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
