@@ -214,12 +214,18 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   // nm: minus row r16's reference maximum (scaled, base 2), the addend of
   // every exponent
   float nm[NT];
+  // thr: the raw logit above which the scaled one passes the reference by
+  // more than kLazyRescale, (kLazyRescale - nm) / sl2 (sl2 > 0), so that each
+  // step tests its raw maximum with one compare
+  const float inv_sl2 = 1.0f / sl2;
+  float thr[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[t][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     nm[t] = -kNegBig;
+    thr[t] = (kLazyRescale + kNegBig) * inv_sl2;
   }
   uint4 ones = make_uint4(Mth::kOnes, Mth::kOnes, Mth::kOnes, Mth::kOnes);
   // kept in registers (as a known constant the compiler rebuilds it with
@@ -326,6 +332,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const float mnew = bm > mold + kLazyRescale ? bm : mold;
     const float alpha = fast_exp2(mold - mnew);
     nm[t] = -mnew;
+    thr[t] = (kLazyRescale + mnew) * inv_sl2;
     // output rows 4*q4+i take the factor of the lane that holds row 4*q4+i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -377,9 +384,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         }
       }
       // raise the reference only where a scaled logit passes it by more than
-      // kLazyRescale (sl2 > 0, so the raw maximum scales to the scaled one)
+      // kLazyRescale: the raw maximum against thr (sl2 > 0, so the raw
+      // maximum scales to the scaled one)
       const float mx = max8(z);
-      if (__any(__builtin_fmaf(mx, sl2, nm[t]) > kLazyRescale)) rescale(t, mx);
+      if (__any(mx > thr[t])) rescale(t, mx);
       accumulate(t, z, vf);
     }
   };
