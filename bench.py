@@ -321,6 +321,26 @@ class DecodeSetup:
             self.call(li)
 
 
+def multi_query_bytes(torch, wl, num_query_tokens):
+    """(logical K/V bytes, algorithmic bytes) of one multi-query call: unique
+    K/V rows (shared prefix blocks once), the T query rows read and T output
+    rows written, the used table entries, the lengths and the query offsets."""
+    lens = wl.context_lens.to(torch.int64)
+    S, Hq, Hkv, D, e = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 2
+    kv_logical = int(lens.sum()) * Hkv * D * e * 2
+    kv_unique = unique_token_rows(wl) * Hkv * D * e * 2
+    alg = (kv_unique + 2 * num_query_tokens * Hq * D * e + int(((lens + 15) // 16).sum()) * 4
+           + S * 4 + (S + 1) * 4)
+    return kv_logical, alg
+
+
+def prefill_flops(num_prompts, prompt_len, num_q_heads, head_dim):
+    """Matrix flops of causal prefill attention: token t of a prompt meets
+    t + 1 keys; 2 flop per multiply-add, for QK and for PV."""
+    L = prompt_len
+    return 4 * head_dim * num_q_heads * num_prompts * (L * (L + 1) // 2)
+
+
 def decode_bytes(torch, wl, fused):
     """Byte accounting of one decode call (per layer), from the workload's
     structure: logical and unique K/V rows, q and out, used table entries and
@@ -485,12 +505,7 @@ def run_multi_query(args, torch, np, mvk, W, wl, layers, nsets, nlayers_step, bt
             torch, dev, [lambda li=li: call_unplanned(li) for li in range(len(layers))], reps)
     ms_per_step = (per_call_us * nlayers_step + (plan_us or 0.0)) / 1e3
 
-    lens = wl.context_lens.to(torch.int64)
-    e = 2
-    kv_logical = int(lens.sum()) * Hkv * D * e * 2
-    kv_unique = unique_token_rows(wl) * Hkv * D * e * 2
-    alg = (kv_unique + 2 * T * Hq * D * e + int(((lens + 15) // 16).sum()) * 4 + S * 4
-           + (S + 1) * 4)
+    kv_logical, alg = multi_query_bytes(torch, wl, T)
     step_s = ms_per_step / 1e3
     achieved = alg / (per_call_us * 1e-6) / 1e9
     result = {
@@ -562,8 +577,7 @@ def run_prefill(args, torch, mvk, W, wl, nlayers_step, dev):
     torch.cuda.synchronize()
     reps = max(1, args.steps // nsets)
     per_call_us = graph_time_per_call(torch, dev, [lambda i=i: call(i) for i in range(nsets)], reps)
-    # causal: token t of a prompt meets t + 1 keys; 2 flop per multiply-add, QK and PV
-    flops = 4 * D * Hq * S * (L * (L + 1) // 2)
+    flops = prefill_flops(S, L, Hq, D)
     tflops = flops / (per_call_us * 1e-6) / 1e12
     peak = MFMA_PEAK_TFLOPS[wl.dtype]
     T = S * L
