@@ -103,6 +103,34 @@ def test_planned_short_descriptors_at_capacity(fused):
     check_layer(wl, 0, fused, "short descriptors at capacity")
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused_write"])
+def test_planned_at_the_ranking_capacity(fused):
+    """1024 sequences, the most one plan ranks (every workgroup holds all
+    their keys in LDS), with ties, one-token contexts and longer ones."""
+    gen = torch.Generator().manual_seed(1024)
+    lens = torch.randint(1, 97, (1024,), generator=gen)
+    lens[::7] = 48                                   # ties
+    lens[3::17] = 1
+    lens[5::101] = 700
+    wl = W.make_custom("p", "f16", lens.tolist(), 8, 2, 64, int(((lens + 15) // 16).sum()) + 3,
+                       1024)
+    assert mvk.plan_size(1024, 8, 2, 64, wl.max_context_len) is not None
+    assert mvk.plan_size(1025, 8, 2, 64, wl.max_context_len) is None
+    check_layer(wl, 0, fused, "1024 sequences")
+
+
+def test_planned_at_the_kv_head_capacity():
+    """256 KV heads (the most a plan takes), g = 1 and g = 2: item i's head
+    is i mod 256 through the multiply-high division."""
+    for hq, D, dtype in ((256, 64, "bf16"), (512, 128, "f16")):
+        lens = [1, 40, 333, 16, 17]
+        wl = W.make_custom("p", dtype, lens, hq, 256, D, sum(-(-L // 16) for L in lens) + 2,
+                           hq + D)
+        assert mvk.plan_size(len(lens), hq, 256, D, wl.max_context_len) is not None
+        assert mvk.plan_size(len(lens), 2 * 257, 257, D, wl.max_context_len) is None
+        check_layer(wl, 0, True, f"256 KV heads, g = {hq // 256}")
+
+
 @pytest.mark.parametrize("dtype,D,hq,hkv", [("bf16", 128, 8, 8), ("f16", 64, 32, 4)])
 def test_planned_items_longer_than_one_descriptor(dtype, D, hq, hkv):
     """Contexts past 56 blocks (one wave descriptor) up to the planned path's
