@@ -84,6 +84,16 @@ def test_more_items_than_resident_bins():
     parity(wl, q, qs)
 
 
+def test_at_the_ranking_capacity():
+    """1024 sequences (the most one plan ranks), g = 4, 0-4 new tokens each
+    (up to the 16-row tile), every row against the oracle."""
+    gen = torch.Generator().manual_seed(4096)
+    lens = torch.randint(1, 120, (1024,), generator=gen).tolist()
+    news = capped(torch.randint(0, 5, (1024,), generator=gen).tolist(), lens, 4)
+    wl, q, qs = mq_case("bf16", lens, news, 8, 2, 64, seed=4097)
+    parity(wl, q, qs)
+
+
 def test_speculative_verification_qwen3_shape():
     """The benchmark's Qwen3-shaped step with 4 draft tokens (5 new tokens per
     sequence), full size, every sequence checked."""
